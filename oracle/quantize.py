@@ -1,0 +1,46 @@
+"""Per-token int8 quantizer reference, numpy float32 (test infrastructure only).
+
+fkl.flash_attention PR ("FA-2 forward with fused epilogue + compressed int8 KV
+cache"), Summary: compress_kv() quantizes each token to int8 with one fp32
+scale per token, for a bounded (~1e-3) error.  The page gives neither the
+scale rule, the rounding nor the clamp; readings used here:
+
+* Symmetric absmax scaling, the plainest reading of a single fp32 scale for
+  each token: the token's largest magnitude maps to code 127,
+  s = fp32(absmax) / fp32(127), one IEEE fp32 division.
+* q = rint(x / s) with the IEEE fp32 quotient (not a reciprocal product),
+  rounding half to even, clamped to [-127, 127]; -128 is never produced.
+* An all-zero token gets s = 0 and q = 0 (no division by zero).
+
+Computed in float32 on purpose: the quantized codes are an integer decision
+taken in fp32, the precision the library takes it in, so both sides can agree
+bit for bit.
+
+compression_ratio: fkl PR, Verification (the KV compression-ratio check,
+3.76x at head_dim 64 against a 3.5x threshold) -- bytes of an fp32 token (4d)
+over bytes of its int8 codes plus the fp32 scale (d + 4).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["quantize_per_token", "compression_ratio"]
+
+
+def quantize_per_token(x) -> tuple[np.ndarray, np.ndarray]:
+    """x: float array (..., d) (float32 or values exactly representable in it).
+    Returns (codes int8 (..., d), scales float32 (...))."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.max(np.abs(x), axis=-1)                          # exact in fp32
+    s = (a / np.float32(127.0)).astype(np.float32)          # IEEE fp32 division
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = np.rint(x / safe[..., None])                     # fp32 quotient, half-to-even
+    r = np.clip(r, -127, 127)
+    r = np.where((s > 0)[..., None], r, 0.0)
+    return r.astype(np.int8), s.astype(np.float32)
+
+
+def compression_ratio(head_dim: int, src_bytes_per_elem: int = 4) -> float:
+    """Bytes of an uncompressed token over bytes of its int8 codes + one fp32 scale."""
+    return (src_bytes_per_elem * head_dim) / (head_dim + 4)

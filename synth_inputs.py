@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs shared by the oracle-side tests, the GPU tests and bench.py.
+
+This module draws random numbers and rounds them to the storage dtypes the
+workloads name; it contains none of the attention or quantization arithmetic.
+Both the CPU oracle and the HIP path consume exactly the arrays produced here.
+
+Workloads (the five configurations the measurements and parity tests use):
+
+  c1  causal fp32 self-attention, bh=2, s_q=s_k=128, d=64
+  c2  ragged non-causal fp32, bh=8, s_q=33, s_k=127, d=32 (+ epilogue x*2.0+0.5)
+  c3  int8-KV causal prefill, batch 4 x 32 heads, s=4096, d=128; Q bf16, K/V fp32
+      (to be compressed per token), bf16 output
+  c4  GQA decode, batch 16, 32 query / 8 KV heads, s_q=1, s_k=32768, d=128;
+      Q bf16, K/V fp32 (to be compressed per token), fp32 output
+  c5  GQA causal prefill bf16, batch 1, 64 query / 8 KV heads, s=32768, d=128;
+      run with no window and with a 4096-token window
+
+Recipe: config cN uses numpy Generator(PCG64(N)) and draws Q, then K, then V
+as float32 standard normals in (batch*heads, seq, head_dim) layout.  Where the
+workload says bf16, the float32 draw is rounded to bf16 (round to nearest even)
+and both sides consume the rounded values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "draw_qkv", "f32_to_bf16_bits",
+           "bf16_bits_to_f32", "round_bf16", "rng_normal"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    bh_q: int
+    bh_kv: int
+    s_q: int
+    s_k: int
+    d: int
+    causal: bool
+    window: int          # 0 = no band
+    q_dtype: str         # "f32" | "bf16"
+    kv_dtype: str        # "f32" | "bf16" | "i8" (i8: drawn as f32, compressed by the library)
+    out_dtype: str       # "f32" | "bf16"
+
+    @property
+    def group(self) -> int:
+        return self.bh_q // self.bh_kv
+
+
+WORKLOADS = {
+    "c1": Workload("c1_causal_f32_bh2_s128_d64", 1, 2, 2, 128, 128, 64, True, 0, "f32", "f32", "f32"),
+    "c2": Workload("c2_ragged_f32_bh8_sq33_sk127_d32", 2, 8, 8, 33, 127, 32, False, 0, "f32", "f32", "f32"),
+    "c3": Workload("c3_int8kv_causal_b4h32_s4096_d128", 3, 128, 128, 4096, 4096, 128, True, 0, "bf16", "i8", "bf16"),
+    "c4": Workload("c4_gqa_decode_b16_h32kv8_sk32768_d128", 4, 512, 128, 1, 32768, 128, False, 0, "bf16", "i8", "f32"),
+    "c5": Workload("c5_gqa_causal_bf16_h64kv8_s32768_d128", 5, 64, 8, 32768, 32768, 128, True, 0, "bf16", "bf16", "bf16"),
+    "c5w": Workload("c5w_gqa_window4096_bf16_h64kv8_s32768_d128", 5, 64, 8, 32768, 32768, 128, True, 4096, "bf16", "bf16", "bf16"),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 exactly."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 array whose values are exactly representable in bfloat16 (RNE of x)."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def rng_normal(seed: int, *shapes):
+    """Standard-normal float32 arrays drawn in order from Generator(PCG64(seed))."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return [g.standard_normal(size=s, dtype=np.float32) for s in shapes]
+
+
+def draw_qkv(w: Workload, bh_kv: int | None = None, s_q: int | None = None,
+             s_k: int | None = None, seed: int | None = None):
+    """Q, K, V float32 arrays for a workload (Q rounded to bf16 values when q_dtype is bf16,
+    K/V rounded when kv_dtype is bf16).  bh_kv / s_q / s_k / seed may change the draw for
+    reduced cases; the draw order (Q, then K, then V) is fixed."""
+    bh_kv = w.bh_kv if bh_kv is None else bh_kv
+    s_q = w.s_q if s_q is None else s_q
+    s_k = w.s_k if s_k is None else s_k
+    seed = w.seed if seed is None else seed
+    bh_q = bh_kv * w.group
+    q, k, v = rng_normal(seed, (bh_q, s_q, w.d), (bh_kv, s_k, w.d), (bh_kv, s_k, w.d))
+    if w.q_dtype == "bf16":
+        q = round_bf16(q)
+    if w.kv_dtype == "bf16":
+        k = round_bf16(k)
+        v = round_bf16(v)
+    return q, k, v

@@ -1,0 +1,361 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* brute force in pure Python (math.exp / math.fsum) on tiny inputs,
+* torch's scaled_dot_product_attention in float64 on the CPU with an explicit mask,
+* invariants of softmax attention and closed forms,
+* the values the pages print (tests/golden/printed_values.json),
+* exact-arithmetic checks of the quantizer's IEEE fp32 decisions.
+
+None of these tests needs a GPU.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from synth_inputs import rng_normal
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- brute force
+def brute_attention(q, k, v, causal, window, scale, group, ops=(), ks=None, vs=None):
+    """Pure-Python loops; exact sums via math.fsum.  Independent of numpy linear algebra."""
+    bh_q, s_q, d = len(q), len(q[0]), len(q[0][0])
+    s_k = len(k[0])
+    out = [[[0.0] * d for _ in range(s_q)] for _ in range(bh_q)]
+    lse = [[0.0] * s_q for _ in range(bh_q)]
+    for h in range(bh_q):
+        g = h // group
+        kk = [[float(k[g][j][c]) * (float(ks[g][j]) if ks is not None else 1.0) for c in range(d)]
+              for j in range(s_k)]
+        vv = [[float(v[g][j][c]) * (float(vs[g][j]) if vs is not None else 1.0) for c in range(d)]
+              for j in range(s_k)]
+        for i in range(s_q):
+            ia = i + s_k - s_q
+            keys = [j for j in range(s_k)
+                    if (not causal or j <= ia) and (window == 0 or j > ia - window)]
+            if not keys:
+                out[h][i] = [0.0] * d
+                lse[h][i] = -math.inf
+                continue
+            sc = {j: scale * math.fsum(float(q[h][i][c]) * kk[j][c] for c in range(d)) for j in keys}
+            m = max(sc.values())
+            w = {j: math.exp(sc[j] - m) for j in keys}
+            z = math.fsum(w.values())
+            row = [math.fsum(w[j] * vv[j][c] for j in keys) / z for c in range(d)]
+            for kind, val in ops:
+                row = [x * val if kind == "mul" else x + val for x in row]
+            out[h][i] = row
+            lse[h][i] = m + math.log(z)
+    return np.array(out), np.array(lse)
+
+
+TINY = [
+    # bh_q, bh_kv, s_q, s_k, d, causal, window
+    (1, 1, 1, 1, 1, False, 0),
+    (2, 2, 3, 5, 2, False, 0),
+    (2, 2, 4, 4, 4, True, 0),
+    (3, 1, 2, 6, 4, True, 0),       # GQA + ragged causal
+    (4, 2, 5, 6, 2, True, 2),       # window
+    (2, 1, 6, 6, 32, True, 3),
+    (2, 2, 3, 6, 1, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", TINY)
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_oracle_matches_brute_force(case, seed):
+    bh_q, bh_kv, s_q, s_k, d, causal, window = case
+    q, k, v = rng_normal(seed, (bh_q, s_q, d), (bh_kv, s_k, d), (bh_kv, s_k, d))
+    scale = 1.0 / math.sqrt(d)
+    ops = [("mul", 2.0), ("add", 0.5)] if seed == 12 else []
+    o_ref, l_ref = brute_attention(q.tolist(), k.tolist(), v.tolist(), causal, window, scale,
+                                   bh_q // bh_kv, ops)
+    o, l = oracle.attention(q, k, v, causal=causal, window=window, epilogue=ops)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_oracle_int8_matches_brute_force(seed):
+    bh_q, bh_kv, s_q, s_k, d = 4, 2, 3, 7, 4
+    q, k, v = rng_normal(seed, (bh_q, s_q, d), (bh_kv, s_k, d), (bh_kv, s_k, d))
+    g = np.random.default_rng(seed)
+    kq = g.integers(-127, 128, size=(bh_kv, s_k, d)).astype(np.int8)
+    vq = g.integers(-127, 128, size=(bh_kv, s_k, d)).astype(np.int8)
+    ks = (np.abs(k[..., 0]) / 127).astype(np.float32)
+    vs = (np.abs(v[..., 0]) / 127).astype(np.float32)
+    o_ref, l_ref = brute_attention(q.tolist(), kq.tolist(), vq.tolist(), True, 0, 0.5,
+                                   bh_q // bh_kv, (), ks.tolist(), vs.tolist())
+    o, l = oracle.attention(q, kq, vq, causal=True, scale=0.5, k_scale=ks, v_scale=vs)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-13)
+
+
+def test_empty_rows_give_zero_and_neg_inf_lse():
+    # causal with s_q > s_k leaves the first s_q - s_k rows without a visible key
+    q, k, v = rng_normal(5, (1, 5, 4), (1, 3, 4), (1, 3, 4))
+    o, l = oracle.attention(q, k, v, causal=True)
+    ob, lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), True, 0, 0.5, 1)
+    assert np.all(o[0, :2] == 0) and np.all(np.isneginf(l[0, :2]))
+    np.testing.assert_allclose(o, ob, atol=1e-13, rtol=0)
+
+
+# ----------------------------------------------------------------------------- library cross-check
+@pytest.mark.parametrize("case", [
+    (4, 4, 33, 127, 32, False, 0),
+    (8, 2, 64, 64, 64, True, 0),
+    (4, 1, 40, 100, 128, True, 0),
+    (2, 2, 50, 90, 64, True, 17),
+])
+def test_oracle_matches_torch_sdpa_fp64(case):
+    torch = pytest.importorskip("torch")
+    bh_q, bh_kv, s_q, s_k, d, causal, window = case
+    q, k, v = rng_normal(7, (bh_q, s_q, d), (bh_kv, s_k, d), (bh_kv, s_k, d))
+    o, l = oracle.attention(q, k, v, causal=causal, window=window)
+    G = bh_q // bh_kv
+    kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(G, dim=0)
+    vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(G, dim=0)
+    qt = torch.from_numpy(q.astype(np.float64))
+    # explicit boolean mask built here (bottom-right alignment), not torch's top-left is_causal
+    i = torch.arange(s_q)[:, None] + (s_k - s_q)
+    j = torch.arange(s_k)[None, :]
+    m = torch.ones(s_q, s_k, dtype=torch.bool)
+    if causal:
+        m &= j <= i
+    if window:
+        m &= j > i - window
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    sc = torch.einsum("hid,hjd->hij", qt, kt) / math.sqrt(d)
+    sc = sc.masked_fill(~m, -math.inf)
+    np.testing.assert_allclose(l, torch.logsumexp(sc, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- invariants
+def test_softmax_rows_sum_to_one_and_nonnegative():
+    # with V = identity the output rows are the softmax rows themselves
+    s_q, s_k = 9, 13
+    q, k = rng_normal(3, (2, s_q, 8), (2, s_k, 8))
+    v = np.broadcast_to(np.eye(s_k), (2, s_k, s_k)).copy()
+    qq = np.concatenate([q, np.zeros((2, s_q, s_k - 8))], axis=2)
+    kk = np.concatenate([k, np.zeros((2, s_k, s_k - 8))], axis=2)
+    for causal, window in [(False, 0), (True, 0), (True, 4)]:
+        p, _ = oracle.attention(qq, kk, v, causal=causal, window=window, scale=0.3)
+        assert np.all(p >= 0)
+        np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+        vis = oracle.visible_mask(s_q, s_k, causal, window)
+        assert np.all(p[:, ~vis] == 0)
+
+
+def test_causal_rows_ignore_future_keys_bitwise():
+    s = 24
+    q, k, v = rng_normal(4, (3, s, 16), (3, s, 16), (3, s, 16))
+    o1, l1 = oracle.attention(q, k, v, causal=True)
+    k2, v2 = k.copy(), v.copy()
+    cut = 10
+    k2[:, cut + 1:] = rng_normal(99, k2[:, cut + 1:].shape)[0]
+    v2[:, cut + 1:] = 1e3
+    o2, l2 = oracle.attention(q, k2, v2, causal=True)
+    assert np.array_equal(o1[:, :cut + 1], o2[:, :cut + 1])
+    assert np.array_equal(l1[:, :cut + 1], l2[:, :cut + 1])
+    assert not np.allclose(o1[:, cut + 1:], o2[:, cut + 1:])
+
+
+def test_output_is_convex_combination_of_visible_values():
+    s_q, s_k, d = 12, 20, 8
+    q, k, v = rng_normal(6, (2, s_q, d), (2, s_k, d), (2, s_k, d))
+    o, _ = oracle.attention(q, k, v, causal=True, window=5)
+    vis = oracle.visible_mask(s_q, s_k, True, 5)
+    for h in range(2):
+        for i in range(s_q):
+            vv = v[h][vis[i]]
+            assert np.all(o[h, i] >= vv.min(0) - 1e-12) and np.all(o[h, i] <= vv.max(0) + 1e-12)
+
+
+def test_noncausal_key_permutation_invariance():
+    q, k, v = rng_normal(8, (2, 7, 16), (2, 31, 16), (2, 31, 16))
+    perm = np.random.default_rng(0).permutation(31)
+    o1, l1 = oracle.attention(q, k, v, causal=False)
+    o2, l2 = oracle.attention(q, k[:, perm], v[:, perm], causal=False)
+    np.testing.assert_allclose(o1, o2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l1, l2, atol=1e-13, rtol=0)
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    G = 4
+    q, k, v = rng_normal(9, (8, 10, 16), (2, 10, 16), (2, 10, 16))
+    o1, _ = oracle.attention(q, k, v, causal=True)
+    o2, _ = oracle.attention(q, np.repeat(k, G, 0), np.repeat(v, G, 0), causal=True)
+    assert np.array_equal(o1, o2)
+    # and a wrong head grouping (interleaved) would differ
+    o3, _ = oracle.attention(q, np.tile(k, (G, 1, 1)), np.tile(v, (G, 1, 1)), causal=True)
+    assert not np.allclose(o1, o3)
+
+
+def test_window_at_least_sk_equals_causal():
+    q, k, v = rng_normal(10, (2, 9, 8), (2, 15, 8), (2, 15, 8))
+    oc, _ = oracle.attention(q, k, v, causal=True)
+    for w in (15, 16, 100):
+        ow, _ = oracle.attention(q, k, v, causal=True, window=w)
+        assert np.array_equal(oc, ow)
+
+
+def test_window_one_selects_the_diagonal_value():
+    s_q, s_k = 6, 11
+    q, k, v = rng_normal(12, (2, s_q, 8), (2, s_k, 8), (2, s_k, 8))
+    o, l = oracle.attention(q, k, v, causal=True, window=1)
+    for i in range(s_q):
+        np.testing.assert_allclose(o[:, i], v[:, i + s_k - s_q], atol=1e-15, rtol=0)
+        np.testing.assert_allclose(l[:, i], (q[:, i].astype(np.float64) * k[:, i + s_k - s_q]).sum(-1)
+                                   / math.sqrt(8), atol=1e-12, rtol=0)
+
+
+def test_single_key_returns_v0():
+    q, k, v = rng_normal(13, (3, 4, 8), (3, 1, 8), (3, 1, 8))
+    o, _ = oracle.attention(q, k, v, causal=False)
+    np.testing.assert_allclose(o, np.broadcast_to(v, o.shape), atol=1e-15, rtol=0)
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    s_q, s_k = 5, 9
+    _, k, v = rng_normal(14, (1,), (2, s_k, 8), (2, s_k, 8))
+    q = np.zeros((2, s_q, 8), np.float32)
+    o, l = oracle.attention(q, k, v, causal=True, window=3)
+    vis = oracle.visible_mask(s_q, s_k, True, 3)
+    for i in range(s_q):
+        np.testing.assert_allclose(o[:, i], v[:, vis[i]].astype(np.float64).mean(1), atol=1e-14, rtol=0)
+        np.testing.assert_allclose(l[:, i], math.log(vis[i].sum()), atol=1e-14, rtol=0)
+
+
+def test_two_keys_closed_form():
+    # out = v0 + (v1 - v0) * sigmoid(s1 - s0)
+    q, k, v = rng_normal(15, (1, 1, 4), (1, 2, 4), (1, 2, 4))
+    o, _ = oracle.attention(q, k, v, causal=False, scale=0.7)
+    s = [0.7 * sum(float(q[0, 0, c]) * float(k[0, j, c]) for c in range(4)) for j in range(2)]
+    sig = 1.0 / (1.0 + math.exp(-(s[1] - s[0])))
+    ref = v[0, 0].astype(np.float64) + (v[0, 1].astype(np.float64) - v[0, 0]) * sig
+    np.testing.assert_allclose(o[0, 0], ref, atol=1e-14, rtol=0)
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    s = 40
+    q, k, v = rng_normal(16, (4, s, 16), (2, s, 16), (2, s, 16))
+    o, l = oracle.attention(q, k, v, causal=True)
+    od, ld = oracle.decode(q[:, -1:], k, v)
+    # equal up to BLAS blocking of a one-row vs a many-row product
+    np.testing.assert_allclose(od[:, 0], o[:, -1], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(ld[:, 0], l[:, -1], atol=1e-14, rtol=0)
+    ow, _ = oracle.attention(q, k, v, causal=True, window=7)
+    odw, _ = oracle.decode(q[:, -1:], k, v, window=7)
+    np.testing.assert_allclose(odw[:, 0], ow[:, -1], atol=1e-14, rtol=0)
+
+
+def test_row_and_head_subsets_match_full_computation():
+    q, k, v = rng_normal(17, (4, 300, 8), (2, 300, 8), (2, 300, 8))
+    o, l = oracle.attention(q, k, v, causal=True)
+    rows = [0, 7, 255, 256, 299]
+    os_, ls_ = oracle.attention(q, k, v, causal=True, heads=[1, 3], rows=rows)
+    np.testing.assert_allclose(os_[[1, 3]][:, rows], o[[1, 3]][:, rows], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(ls_[[1, 3]][:, rows], l[[1, 3]][:, rows], atol=1e-14, rtol=0)
+    assert np.isnan(os_[0]).all()
+
+
+def test_epilogue_order_and_values():
+    x = np.array([[-1.0, 0.25, 3.0]])
+    np.testing.assert_array_equal(oracle.apply_epilogue(x, [("mul", 2.0), ("add", 0.5)]), 2 * x + 0.5)
+    np.testing.assert_array_equal(oracle.apply_epilogue(x, [("add", 0.5), ("mul", 2.0)]), 2 * x + 1.0)
+    np.testing.assert_array_equal(oracle.apply_epilogue(x, []), x)
+    with pytest.raises(ValueError):
+        oracle.apply_epilogue(x, [("relu", 0.0)])
+
+
+def test_window_without_causal_rejected():
+    with pytest.raises(ValueError):
+        oracle.visible_mask(3, 3, False, 2)
+
+
+# ----------------------------------------------------------------------------- dequantize
+def test_dequantize_is_exact_product():
+    g = np.random.default_rng(1)
+    qv = g.integers(-127, 128, size=(3, 5, 7)).astype(np.int8)
+    s = g.random((3, 5)).astype(np.float32)
+    dq = oracle.dequantize(qv, s)
+    for idx in np.ndindex(qv.shape):
+        exact = Fraction(int(qv[idx])) * Fraction(float(s[idx[:2]]))
+        assert Fraction(float(dq[idx])) == exact
+
+
+# ----------------------------------------------------------------------------- quantizer
+def _nearest_f32(fr: Fraction) -> np.float32:
+    """Round an exact rational to the nearest float32 (ties to even), by exhaustive neighbourhood."""
+    approx = np.float32(float(fr))
+    cands = [np.nextafter(approx, np.float32(-np.inf)), approx, np.nextafter(approx, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                      int(np.array(c, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_quantizer_hand_vector():
+    hv = json.load(open(os.path.join(GOLDEN, "quantizer_hand_vector.json")))
+    x = np.array(hv["x"], np.float32)[None]
+    q, s = oracle.quantize_per_token(x)
+    assert s[0] == np.float32(hv["scale"])
+    assert q[0].tolist() == hv["codes"]
+
+
+def test_quantizer_scale_and_codes_follow_ieee_fp32_decisions():
+    x = rng_normal(31, (64, 48))[0] * np.float32(3.0)
+    q, s = oracle.quantize_per_token(x)
+    for r in range(x.shape[0]):
+        a = max(abs(Fraction(float(t))) for t in x[r])
+        s_ref = _nearest_f32(a / 127)
+        assert s[r] == s_ref
+        for c in range(0, x.shape[1], 5):
+            quot = _nearest_f32(Fraction(float(x[r, c])) / Fraction(float(s_ref)))
+            code = max(-127, min(127, round(Fraction(float(quot)))))   # round(): half to even
+            assert int(q[r, c]) == code
+
+
+def test_quantizer_bounds_and_extremes():
+    x = rng_normal(32, (200, 128))[0]
+    x[3] = 0.0
+    x[4, :] = 1e-30
+    x[5, 7] = -50.0
+    q, s = oracle.quantize_per_token(x)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    assert s[3] == 0 and np.all(q[3] == 0)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-6))
+    amax = np.argmax(np.abs(x), axis=1)
+    nz = s > 0
+    assert np.all(np.abs(q[np.arange(200), amax].astype(int))[nz] == 127)
+    assert q[5, 7] == -127
+
+
+def test_compression_ratio_matches_printed_value():
+    gv = json.load(open(os.path.join(GOLDEN, "printed_values.json")))
+    c = gv["compression_ratio_d64"]
+    r = oracle.compression_ratio(c["head_dim"])
+    assert round(r, c["digits"]) == c["printed"] and r > c["threshold"]
+    assert abs(r - 64 * 4 / 68) < 1e-15
+    big = oracle.compression_ratio(1 << 20)
+    assert abs(big - gv["capacity_limit"]["printed"]) < 1e-4
+
+
+def test_quantization_error_is_bounded_like_the_pages_claim():
+    # fkl PR, Summary: int8 KV for a bounded error of order 1e-3 on the attention output
+    w = 256
+    q, k, v = rng_normal(33, (4, 1, 64), (4, w, 64), (4, w, 64))
+    kq, ks = oracle.quantize_per_token(k)
+    vq, vs = oracle.quantize_per_token(v)
+    o_ref, _ = oracle.decode(q, k, v)
+    o_q, _ = oracle.decode(q, kq, vq, k_scale=ks, v_scale=vs)
+    err = np.abs(o_ref - o_q).max()
+    assert 1e-4 < err < 1e-2
