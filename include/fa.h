@@ -1,0 +1,155 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library with a per-token
+ * int8 KV cache.
+ *
+ * The operations and where they are defined:
+ *   fa_compress_kv  -- per-token int8 quantization with one fp32 scale per token
+ *                      (fkl.flash_attention PR, "FA-2 forward with fused epilogue +
+ *                      compressed int8 KV cache", Summary: compress_kv()).
+ *   fa_forward      -- exact softmax(Q K^T * scale) V as a FlashAttention-2 style
+ *                      forward with causal / ragged / GQA / sliding-window masks, the
+ *                      Mul/Add epilogue chain and int8 K/V dequantized inside q.k and
+ *                      p.v (fkl PR, Summary: flash_attention(), epilogue=[...], layout
+ *                      and precision bullet; SKaiNET PR #419, Summary: GQA groups and
+ *                      sliding-window layers).
+ *   fa_decode       -- one query row per head against an int8 cache, split over the
+ *                      keys with a log-sum-exp merge of the partial (m, l, O) states
+ *                      (fkl PR, Verification: the decode check; kernbench2 ADR-0060
+ *                      commit: split decode with a reduce of running (m, l, O)).
+ *
+ * Conventions shared by every entry point
+ *   Layout      (batch*heads, seq, head_dim), row-major and contiguous; head_dim is a
+ *               multiple of 32 and at most FA_MAX_HEAD_DIM (fkl PR, Summary).
+ *   Pointers    device pointers unless stated; 16-byte aligned.  The caller allocates
+ *               and owns every buffer; the library allocates no device memory and keeps
+ *               no pointer after a call returns.
+ *   Streams     `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *               asynchronously; nothing synchronises the host.
+ *   Errors      every argument is checked on the host before anything is enqueued.  On
+ *               error a negative fa_status is returned, nothing is enqueued or written,
+ *               and fa_last_error() gives the reason on the calling thread.
+ *               No exception or abort crosses the ABI.
+ *   Precision   accumulation is fp32 everywhere (fkl PR, Summary).
+ *   GQA         G = bh_q / bh_kv must be an integer; query head h reads KV head h / G.
+ *   Causal      bottom-right aligned: query row i sees key j iff j <= i + (s_k - s_q).
+ *   Window      W > 0 keeps keys with i' - W < j <= i' (W counts the diagonal);
+ *               only together with causal.  W >= s_k is the same as plain causal.
+ *   Empty rows  a query row with no visible key returns 0 (and LSE = -inf).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,      /* null/misaligned pointer, bad size, inconsistent arguments */
+  FA_ERR_UNSUPPORTED = -2,  /* head_dim, dtype combination or epilogue length not supported */
+  FA_ERR_WORKSPACE = -3,    /* decode workspace missing or too small */
+  FA_ERR_HIP = -4           /* the HIP runtime reported an error (text in fa_last_error) */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_I8 = 2 } fa_dtype;
+
+typedef enum { FA_EPI_MUL = 1, FA_EPI_ADD = 2 } fa_epi_kind;
+
+/* One epilogue post-op, applied in fp32 to the normalised attention output, in list order,
+ * before the cast to the output dtype (fkl PR, Summary: epilogue=[Mul(2.0), Add(0.5)]).
+ * Values and the list itself are kernel arguments: changing either never selects another
+ * kernel (fkl PR, Verification: epilogue values change without recompile). */
+typedef struct {
+  int32_t kind;   /* fa_epi_kind */
+  float value;
+} fa_epilogue_op;
+
+#define FA_MAX_EPILOGUE 8
+#define FA_MAX_HEAD_DIM 256
+
+/*
+ * fa_compress_kv -- quantize n_tokens rows of head_dim values to int8 codes + fp32 scales.
+ *   x          device, [n_tokens, head_dim], FA_F32 or FA_BF16 (x_dtype).
+ *   q_out      device, [n_tokens, head_dim] int8.
+ *   scale_out  device, [n_tokens] fp32.
+ * Per token: a = max|x|, s = a / 127 (IEEE fp32 division), q = rint(x / s) (IEEE fp32
+ * quotient, ties to even) clamped to [-127, 127]; an all-zero token gives s = 0, q = 0.
+ * Outputs may not alias x.  n_tokens == 0 is a no-op that returns FA_OK.
+ */
+int fa_compress_kv(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_dim,
+                   int8_t* q_out, float* scale_out, void* stream);
+
+/*
+ * fa_forward -- attention forward for bh_q query heads over bh_kv KV heads.
+ *   q        device, [bh_q, s_q, head_dim], q_dtype FA_F32 or FA_BF16.
+ *   k, v     device, [bh_kv, s_k, head_dim], kv_dtype FA_F32, FA_BF16 or FA_I8.
+ *   k_scale, v_scale  device, [bh_kv, s_k] fp32 per-token scales; required iff kv_dtype is
+ *            FA_I8 (values are then q * s, dequantized in registers), NULL otherwise.
+ *   out      device, [bh_q, s_q, head_dim], out_dtype FA_F32 or FA_BF16 (RNE cast).
+ *   lse_out  device or NULL, [bh_q, s_q] fp32 natural-log log-sum-exp of the scaled scores.
+ *   softmax_scale  <= 0 selects 1/sqrt(head_dim).
+ *   causal, window  see the conventions above; window > 0 requires causal.
+ *   epi, n_epi      host array of n_epi (<= FA_MAX_EPILOGUE) post-ops, may be NULL if 0.
+ * Supported (q_dtype, kv_dtype): (F32, F32), (F32, I8), (BF16, BF16), (BF16, I8).
+ * s_q == 0 is a no-op; s_k == 0 with s_q > 0 writes zeros (every row is empty).
+ */
+int fa_forward(const void* q, int32_t q_dtype,
+               const void* k, const void* v, int32_t kv_dtype,
+               const float* k_scale, const float* v_scale,
+               void* out, int32_t out_dtype, float* lse_out,
+               int32_t bh_q, int32_t bh_kv, int32_t s_q, int32_t s_k, int32_t head_dim,
+               float softmax_scale, int32_t causal, int32_t window,
+               const fa_epilogue_op* epi, int32_t n_epi, void* stream);
+
+/*
+ * fa_decode_num_splits -- the split count fa_decode uses when num_splits == 0.
+ */
+int32_t fa_decode_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim);
+
+/*
+ * fa_decode_workspace_bytes -- device workspace fa_decode needs for these sizes
+ * (num_splits == 0 means the automatic count).  The workspace holds one partial
+ * (m, l, O[head_dim]) per (query head, split), fp32.
+ */
+size_t fa_decode_workspace_bytes(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim,
+                                 int32_t num_splits);
+
+/*
+ * fa_decode -- one decode step: each of the bh_q query heads has one row that sees the whole
+ * int8 cache of its KV head (or its last `window` keys), computed as a split-KV pass that
+ * writes partial (m, l, O) states to `workspace` followed by a log-sum-exp merge pass.
+ *   q        device, [bh_q, 1, head_dim], FA_BF16 or FA_F32.
+ *   k, v     device int8 codes [bh_kv, s_k, head_dim]; k_scale, v_scale device fp32 [bh_kv, s_k].
+ *   out      device, [bh_q, 1, head_dim], FA_F32 or FA_BF16.
+ *   lse_out  device or NULL, [bh_q] fp32.
+ *   num_splits  0 = automatic; otherwise 1..4096.
+ *   workspace   device, at least fa_decode_workspace_bytes(...) bytes, 16-byte aligned.
+ * The result may differ with num_splits only by fp32 rounding.
+ */
+int fa_decode(const void* q, int32_t q_dtype,
+              const int8_t* k, const int8_t* v, const float* k_scale, const float* v_scale,
+              void* out, int32_t out_dtype, float* lse_out,
+              int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim,
+              float softmax_scale, int32_t window, int32_t num_splits,
+              const fa_epilogue_op* epi, int32_t n_epi,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for the last non-OK return on the calling thread ("" if none).  Valid until the
+ * next library call on this thread. */
+const char* fa_last_error(void);
+
+/* Name of the kernel instantiation the last successful launch on this thread used.  It
+ * depends only on dtypes, head_dim and the mask family, never on epilogue values or length. */
+const char* fa_last_kernel(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,246 @@
+"""Exact attention with a per-token int8 KV cache on MI355X (gfx950).
+
+Thin Python binding over the C ABI of libfa.so (include/fa.h): arguments are
+checked for shape and dtype, torch tensors are passed as device pointers with
+the current HIP stream, and every step of the computation runs in the HIP
+kernels.  There is no CPU path: if the library is missing or no GPU is
+present, the calls raise.
+
+    codes, scales = compress_kv(k)                       # int8 + fp32 per token
+    out = flash_attention(q, k, v, causal=True)          # bf16 or fp32
+    out = flash_attention(q, kc, vc, k_scale=ks, v_scale=vs, causal=True,
+                          epilogue=[Mul(2.0), Add(0.5)])
+    out = decode(q1, kc, vc, ks, vs)                     # split-KV decode step
+
+Layout (batch*heads, seq, head_dim), head_dim a multiple of 32 up to 256.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = ["Mul", "Add", "compress_kv", "flash_attention", "decode", "decode_workspace_bytes",
+           "decode_num_splits", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
+           "F32", "BF16", "I8"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+F32, BF16, I8 = 0, 1, 2
+_EPI_MUL, _EPI_ADD = 1, 2
+_MAX_EPI = 8
+
+
+class FAError(RuntimeError):
+    """A non-OK status from the library; .code holds the fa_status value."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fa error {code}: {msg}")
+        self.code = code
+
+
+@dataclass(frozen=True)
+class Mul:
+    """Epilogue op: out = out * value (fp32, applied inside the kernel)."""
+    value: float
+
+
+@dataclass(frozen=True)
+class Add:
+    """Epilogue op: out = out + value (fp32, applied inside the kernel)."""
+    value: float
+
+
+class _EpiOp(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("value", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by int8_compressed_kv_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m int8_compressed_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.fa_compress_kv.argtypes = [vp, i32, i64, i32, vp, vp, vp]
+    L.fa_compress_kv.restype = ctypes.c_int
+    L.fa_forward.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp,
+                             i32, i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(_EpiOp), i32, vp]
+    L.fa_forward.restype = ctypes.c_int
+    L.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
+    L.fa_decode_num_splits.restype = i32
+    L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_decode.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32, i32, i32,
+                            ctypes.POINTER(_EpiOp), i32, vp, ctypes.c_size_t, vp]
+    L.fa_decode.restype = ctypes.c_int
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_last_kernel.argtypes = []
+    L.fa_last_kernel.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = i32
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def last_kernel() -> str:
+    return lib().fa_last_kernel().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise FAError(rc, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.int8:
+        return I8
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _out_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported output dtype {dt}")
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _epilogue(ops):
+    ops = list(ops or [])
+    if len(ops) > _MAX_EPI:
+        raise ValueError(f"at most {_MAX_EPI} epilogue ops")
+    arr = (_EpiOp * max(1, len(ops)))()
+    for i, op in enumerate(ops):
+        if isinstance(op, Mul):
+            arr[i] = _EpiOp(_EPI_MUL, float(op.value))
+        elif isinstance(op, Add):
+            arr[i] = _EpiOp(_EPI_ADD, float(op.value))
+        else:
+            raise TypeError(f"epilogue ops must be Mul or Add, got {op!r}")
+    return arr, len(ops)
+
+
+def compress_kv(x, out=None, scales=None):
+    """Quantize (..., head_dim) fp32/bf16 rows to int8 codes with one fp32 scale per row."""
+    torch = _torch()
+    d = x.shape[-1]
+    n = x.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if out.dtype != torch.int8 or out.shape != x.shape:
+        raise ValueError("codes output must be int8 with the input's shape")
+    if scales.dtype != torch.float32 or scales.shape != x.shape[:-1]:
+        raise ValueError("scales output must be fp32 with the input's leading shape")
+    _check(lib().fa_compress_kv(_dev(x, "x"), _dtype_code(x), n, d, _dev(out, "codes"),
+                                _dev(scales, "scales"), _stream()))
+    return out, scales
+
+
+def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(), k_scale=None,
+                    v_scale=None, out_dtype=None, out=None, return_lse=False):
+    """softmax(Q K^T * scale) V for q (bh_q, s_q, d) over k, v (bh_kv, s_k, d).
+
+    k, v: fp32 / bf16 tensors, or int8 codes with k_scale, v_scale (bh_kv, s_k) fp32.
+    out_dtype defaults to q's dtype.  Returns out, or (out, lse) with return_lse.
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D (batch*heads, seq, head_dim)")
+    bh_q, s_q, d = q.shape
+    bh_kv, s_k, dk = k.shape
+    if dk != d or tuple(v.shape) != (bh_kv, s_k, d):
+        raise ValueError("k and v must have shape (bh_kv, s_k, head_dim) matching q's head_dim")
+    if k.dtype != v.dtype:
+        raise ValueError("k and v must share a dtype")
+    if (k_scale is None) != (v_scale is None):
+        raise ValueError("give both k_scale and v_scale, or neither")
+    if k_scale is not None and (tuple(k_scale.shape) != (bh_kv, s_k) or tuple(v_scale.shape) != (bh_kv, s_k)):
+        raise ValueError("scales must have shape (bh_kv, s_k)")
+    odt = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((bh_q, s_q, d), dtype=odt, device=q.device)
+    lse = torch.empty((bh_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
+    epi, n_epi = _epilogue(epilogue)
+    _check(lib().fa_forward(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dtype_code(k),
+                            _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"),
+                            _out_code(out.dtype), _dev(lse, "lse"), bh_q, bh_kv, s_q, s_k, d,
+                            float(scale) if scale else 0.0, int(bool(causal)), int(window), epi, n_epi,
+                            _stream()))
+    return (out, lse) if return_lse else out
+
+
+def decode_num_splits(bh_q, bh_kv, s_k, head_dim) -> int:
+    return int(lib().fa_decode_num_splits(bh_q, bh_kv, s_k, head_dim))
+
+
+def decode_workspace_bytes(bh_q, bh_kv, s_k, head_dim, num_splits=0) -> int:
+    return int(lib().fa_decode_workspace_bytes(bh_q, bh_kv, s_k, head_dim, num_splits))
+
+
+def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epilogue=(),
+           out_dtype=None, out=None, workspace=None, return_lse=False):
+    """One decode step: q (bh_q, 1, d) against the int8 cache k, v (bh_kv, s_k, d) with fp32
+    per-token scales (bh_kv, s_k).  Output fp32 by default."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[1] != 1:
+        raise ValueError("q must have shape (bh_q, 1, head_dim)")
+    bh_q, _, d = q.shape
+    bh_kv, s_k, dk = k.shape
+    if dk != d or tuple(v.shape) != (bh_kv, s_k, d):
+        raise ValueError("k and v must have shape (bh_kv, s_k, head_dim)")
+    if k.dtype != torch.int8 or v.dtype != torch.int8:
+        raise ValueError("decode reads the int8 cache: k and v must be int8 codes")
+    if tuple(k_scale.shape) != (bh_kv, s_k) or tuple(v_scale.shape) != (bh_kv, s_k):
+        raise ValueError("scales must have shape (bh_kv, s_k)")
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((bh_q, 1, d), dtype=odt, device=q.device)
+    need = decode_workspace_bytes(bh_q, bh_kv, s_k, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    lse = torch.empty((bh_q,), dtype=torch.float32, device=q.device) if return_lse else None
+    epi, n_epi = _epilogue(epilogue)
+    _check(lib().fa_decode(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dev(k_scale, "k_scale"),
+                           _dev(v_scale, "v_scale"), _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"),
+                           bh_q, bh_kv, s_k, d, float(scale) if scale else 0.0, int(window), int(num_splits),
+                           epi, n_epi, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                           _stream()))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,242 @@
+// C ABI of the attention library: host-side argument checks, then dispatch to the
+// gfx950 kernels.  Nothing is enqueued when a check fails; the reason is kept in a
+// thread-local string (fa_last_error).  No exception crosses the ABI.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernel_args.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local const char* g_last_kernel = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_head_dim(int32_t d) {
+  if (d <= 0) return fail(FA_ERR_INVALID, "head_dim must be positive (got %d)", d);
+  if (d % 32 != 0 || d > FA_MAX_HEAD_DIM)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim must be a multiple of 32 in [32, %d] (got %d)",
+                FA_MAX_HEAD_DIM, d);
+  return FA_OK;
+}
+
+int fill_epilogue(const fa_epilogue_op* epi, int32_t n_epi, fa::EpiArgs* out) {
+  std::memset(out, 0, sizeof(*out));
+  if (n_epi < 0) return fail(FA_ERR_INVALID, "n_epi must be >= 0 (got %d)", n_epi);
+  if (n_epi > FA_MAX_EPILOGUE)
+    return fail(FA_ERR_UNSUPPORTED, "at most %d epilogue ops are supported (got %d)", FA_MAX_EPILOGUE, n_epi);
+  if (n_epi > 0 && epi == nullptr) return fail(FA_ERR_INVALID, "epi is NULL but n_epi = %d", n_epi);
+  for (int i = 0; i < n_epi; ++i) {
+    if (epi[i].kind != FA_EPI_MUL && epi[i].kind != FA_EPI_ADD)
+      return fail(FA_ERR_INVALID, "epilogue op %d has unknown kind %d", i, epi[i].kind);
+    out->kind[i] = epi[i].kind;
+    out->value[i] = epi[i].value;
+  }
+  out->n = n_epi;
+  return FA_OK;
+}
+
+float resolve_scale(float s, int32_t d) {
+  return s > 0.f ? s : 1.0f / std::sqrt((float)d);
+}
+
+constexpr int32_t kMaxSplits = 4096;
+constexpr int32_t kDecodeTile = 64;   // keys per decode tile
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_version(void) { return 10000; }
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+const char* fa_last_kernel(void) { return g_last_kernel; }
+
+int fa_compress_kv(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_dim, int8_t* q_out,
+                   float* scale_out, void* stream) {
+  g_last_error.clear();
+  if (int r = check_head_dim(head_dim)) return r;
+  if (x_dtype != FA_F32 && x_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "compress_kv input must be FA_F32 or FA_BF16 (got %d)", x_dtype);
+  if (n_tokens < 0) return fail(FA_ERR_INVALID, "n_tokens must be >= 0");
+  if (n_tokens == 0) return FA_OK;
+  if (!x || !q_out || !scale_out) return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(x) || !aligned16(q_out) || (reinterpret_cast<uintptr_t>(scale_out) & 3u))
+    return fail(FA_ERR_INVALID, "x and q_out must be 16-byte aligned, scale_out 4-byte aligned");
+  const char* name = "";
+  hipError_t e = fa::launch_compress(x, x_dtype, n_tokens, head_dim, q_out, scale_out,
+                                     static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "compress_kv launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
+int fa_forward(const void* q, int32_t q_dtype, const void* k, const void* v, int32_t kv_dtype,
+               const float* k_scale, const float* v_scale, void* out, int32_t out_dtype, float* lse_out,
+               int32_t bh_q, int32_t bh_kv, int32_t s_q, int32_t s_k, int32_t head_dim, float softmax_scale,
+               int32_t causal, int32_t window, const fa_epilogue_op* epi, int32_t n_epi, void* stream) {
+  g_last_error.clear();
+  if (int r = check_head_dim(head_dim)) return r;
+  if (bh_q <= 0 || bh_kv <= 0) return fail(FA_ERR_INVALID, "bh_q and bh_kv must be positive");
+  if (bh_q % bh_kv != 0) return fail(FA_ERR_INVALID, "bh_q (%d) must be a multiple of bh_kv (%d)", bh_q, bh_kv);
+  if (s_q < 0 || s_k < 0) return fail(FA_ERR_INVALID, "sequence lengths must be >= 0");
+  if (window < 0) return fail(FA_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && !causal) return fail(FA_ERR_INVALID, "window > 0 requires causal");
+  if (q_dtype != FA_F32 && q_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "q dtype must be FA_F32 or FA_BF16");
+  if (kv_dtype != FA_F32 && kv_dtype != FA_BF16 && kv_dtype != FA_I8)
+    return fail(FA_ERR_UNSUPPORTED, "kv dtype must be FA_F32, FA_BF16 or FA_I8");
+  if (out_dtype != FA_F32 && out_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "out dtype must be FA_F32 or FA_BF16");
+  const bool f32_path = q_dtype == FA_F32 && (kv_dtype == FA_F32 || kv_dtype == FA_I8);
+  const bool bf16_path = q_dtype == FA_BF16 && (kv_dtype == FA_BF16 || kv_dtype == FA_I8);
+  if (!f32_path && !bf16_path)
+    return fail(FA_ERR_UNSUPPORTED, "unsupported (q, kv) dtype pair (%d, %d)", q_dtype, kv_dtype);
+  if (kv_dtype == FA_I8) {
+    if (!k_scale || !v_scale) return fail(FA_ERR_INVALID, "int8 K/V need k_scale and v_scale");
+  } else if (k_scale || v_scale) {
+    return fail(FA_ERR_INVALID, "k_scale/v_scale must be NULL unless kv dtype is FA_I8");
+  }
+  fa::EpiArgs ea;
+  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  if (s_q == 0) return FA_OK;
+  if (!q || !out) return fail(FA_ERR_INVALID, "null q or out");
+  if (s_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "null k or v");
+  if (!aligned16(q) || !aligned16(out) || (s_k > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(FA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+  if ((k_scale && (reinterpret_cast<uintptr_t>(k_scale) & 15u)) ||
+      (v_scale && (reinterpret_cast<uintptr_t>(v_scale) & 15u)) ||
+      (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)))
+    return fail(FA_ERR_INVALID, "scales must be 16-byte aligned and lse_out 4-byte aligned");
+
+  fa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.out = out;
+  a.lse = lse_out;
+  a.bh_q = bh_q;
+  a.bh_kv = bh_kv;
+  a.group = bh_q / bh_kv;
+  a.s_q = s_q;
+  a.s_k = s_k;
+  a.causal = causal ? 1 : 0;
+  a.window = (window > 0 && window < s_k) ? window : 0;   // W >= s_k is plain causal
+  a.out_bf16 = out_dtype == FA_BF16;
+  a.scale = resolve_scale(softmax_scale, head_dim);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.epi = ea;
+  const char* name = "";
+  hipError_t e = f32_path ? fa::launch_prefill_f32(a, head_dim, kv_dtype, static_cast<hipStream_t>(stream), &name)
+                          : fa::launch_prefill_bf16(a, head_dim, kv_dtype, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
+int32_t fa_decode_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim) {
+  (void)head_dim;
+  if (bh_kv <= 0 || bh_q <= 0 || s_k <= 0) return 1;
+  const int32_t group = bh_q / bh_kv;
+  const int32_t col_groups = (group + 3) / 4;   // decode workgroups per (split, KV head)
+  const int64_t units = (int64_t)bh_kv * col_groups;
+  const int32_t tiles = (s_k + kDecodeTile - 1) / kDecodeTile;
+  // aim for ~2048 workgroups, with at least 8 tiles (512 keys) per split
+  int64_t splits = (2048 + units - 1) / units;
+  const int64_t max_by_len = tiles / 8 > 0 ? tiles / 8 : 1;
+  if (splits > max_by_len) splits = max_by_len;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits < 1) splits = 1;
+  return (int32_t)splits;
+}
+
+size_t fa_decode_workspace_bytes(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim, int32_t num_splits) {
+  if (bh_q <= 0 || head_dim <= 0) return 0;
+  if (num_splits <= 0) num_splits = fa_decode_num_splits(bh_q, bh_kv, s_k, head_dim);
+  return (size_t)bh_q * (size_t)num_splits * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+int fa_decode(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, const float* k_scale,
+              const float* v_scale, void* out, int32_t out_dtype, float* lse_out, int32_t bh_q, int32_t bh_kv,
+              int32_t s_k, int32_t head_dim, float softmax_scale, int32_t window, int32_t num_splits,
+              const fa_epilogue_op* epi, int32_t n_epi, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (int r = check_head_dim(head_dim)) return r;
+  if (bh_q <= 0 || bh_kv <= 0) return fail(FA_ERR_INVALID, "bh_q and bh_kv must be positive");
+  if (bh_q % bh_kv != 0) return fail(FA_ERR_INVALID, "bh_q (%d) must be a multiple of bh_kv (%d)", bh_q, bh_kv);
+  if (s_k < 0) return fail(FA_ERR_INVALID, "s_k must be >= 0");
+  if (window < 0) return fail(FA_ERR_INVALID, "window must be >= 0");
+  if (q_dtype != FA_F32 && q_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "decode q must be FA_F32 or FA_BF16");
+  if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "decode out must be FA_F32 or FA_BF16");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(FA_ERR_INVALID, "num_splits must be in [0, %d] (got %d)", kMaxSplits, num_splits);
+  fa::EpiArgs ea;
+  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  if (!q || !out) return fail(FA_ERR_INVALID, "null q or out");
+  if (s_k > 0 && (!k || !v || !k_scale || !v_scale)) return fail(FA_ERR_INVALID, "null k, v or scales");
+  if (!aligned16(q) || !aligned16(out) || (s_k > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(k_scale) ||
+                                                        !aligned16(v_scale))))
+    return fail(FA_ERR_INVALID, "q, k, v, scales and out must be 16-byte aligned");
+  if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)) return fail(FA_ERR_INVALID, "lse_out must be 4-byte aligned");
+  const int32_t splits = num_splits > 0 ? num_splits : fa_decode_num_splits(bh_q, bh_kv, s_k, head_dim);
+  const size_t need = (size_t)bh_q * (size_t)splits * (size_t)(head_dim + 2) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID, "workspace must be 16-byte aligned");
+
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.out = out;
+  a.lse = lse_out;
+  a.partial = static_cast<float*>(workspace);
+  a.bh_q = bh_q;
+  a.bh_kv = bh_kv;
+  a.group = bh_q / bh_kv;
+  a.s_k = s_k;
+  a.key_lo = (window > 0 && window < s_k) ? s_k - window : 0;
+  a.num_splits = splits;
+  const int32_t tiles = (s_k - a.key_lo + kDecodeTile - 1) / kDecodeTile;
+  a.tiles_per_split = (tiles + splits - 1) / splits;
+  a.q_bf16 = q_dtype == FA_BF16;
+  a.out_bf16 = out_dtype == FA_BF16;
+  a.scale = resolve_scale(softmax_scale, head_dim);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.epi = ea;
+  const char* name = "";
+  hipError_t e = fa::launch_decode(a, head_dim, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
+}  // extern "C"

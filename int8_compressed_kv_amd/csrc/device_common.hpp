@@ -1,0 +1,115 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// conversions, cross-lane exchanges and the runtime epilogue interpreter.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernel_args.hpp"
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------------
+// MFMA wrappers (gfx950).  Operand layouts used throughout, for a wave of 64 lanes:
+//   32x32xK: lane l holds A[row l%32][k-slots of half l/32], B[k-slots of half l/32][col l%32];
+//            C[r][c] with c = l%32, r = 8*(i/4) + 4*(l/32) + i%4 for accumulator index i.
+//   16x16xK: lane l holds A[row l%16][k-slots of group l/16], B[...][col l%16];
+//            C[r][c] with c = l%16, r = 4*(l/16) + i.
+// The k-slot assignment is the same function for A and B, so any consistent relabelling
+// of the contraction index between the two operands gives the same product.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma16_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------
+// Conversions
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
+  return __uint_as_float(((unsigned)b) << 16);
+}
+// Two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  bf16x2 p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(unsigned, p);
+}
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  f16x2 p;
+  p[0] = (_Float16)lo;
+  p[1] = (_Float16)hi;
+  return __builtin_bit_cast(unsigned, p);
+}
+// Four signed bytes of w -> two packed bf16x2 (exact: |x| <= 128 fits bf16's 8-bit significand).
+__device__ __forceinline__ u32x2 i8x4_to_bf16x4(unsigned w) {
+  u32x2 r;
+  r[0] = pack_bf16x2((float)(signed char)(w), (float)(signed char)(w >> 8));
+  r[1] = pack_bf16x2((float)(signed char)(w >> 16), (float)(signed char)(w >> 24));
+  return r;
+}
+// Four signed bytes of w -> two packed fp16x2, exact: byte b+128 is placed in the low
+// mantissa bits of fp16 1024.0 (0x6400) and 1152.0 is subtracted.
+__device__ __forceinline__ u32x2 i8x4_to_f16x4(unsigned w) {
+  const unsigned u = w ^ 0x80808080u;
+  f16x2 bias;
+  bias[0] = (_Float16)-1152.0f;
+  bias[1] = (_Float16)-1152.0f;
+  // selector bytes: 4..7 pick from the first operand (0x64646464), 0..3 from u
+  f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u)) + bias;
+  f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u)) + bias;
+  u32x2 r;
+  r[0] = __builtin_bit_cast(unsigned, lo);
+  r[1] = __builtin_bit_cast(unsigned, hi);
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------
+// Cross-lane exchanges
+// ---------------------------------------------------------------------------------------
+// value held by lane l ^ 32
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+__device__ __forceinline__ float xor16(float x) {
+  return __shfl_xor(x, 16, 64);
+}
+
+// ---------------------------------------------------------------------------------------
+// Epilogue: ops applied in list order in fp32, each a separately rounded IEEE operation
+// (no contraction into FMA), so the fused result equals the same ops applied on the host.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float apply_epilogue(float x, const EpiArgs& e) {
+  for (int i = 0; i < e.n; ++i) {
+    const float c = e.value[i];
+    x = (e.kind[i] == kEpiMul) ? __fmul_rn(x, c) : __fadd_rn(x, c);
+  }
+  return x;
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+}  // namespace fa

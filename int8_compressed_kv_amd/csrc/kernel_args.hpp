@@ -1,0 +1,67 @@
+// Plain argument blocks passed by value from the host dispatcher to the kernels,
+// and the host-side launch functions each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kMaxEpilogue = 8;
+constexpr int kEpiMul = 1;
+constexpr int kEpiAdd = 2;
+
+struct EpiArgs {
+  int32_t n;
+  int32_t kind[kMaxEpilogue];
+  float value[kMaxEpilogue];
+};
+
+enum DType : int32_t { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
+struct PrefillArgs {
+  const void* q;        // [bh_q, s_q, d]
+  const void* k;        // [bh_kv, s_k, d]
+  const void* v;        // [bh_kv, s_k, d]
+  const float* k_scale; // [bh_kv, s_k] or null
+  const float* v_scale; // [bh_kv, s_k] or null
+  void* out;            // [bh_q, s_q, d]
+  float* lse;           // [bh_q, s_q] or null
+  int32_t bh_q, bh_kv, group;
+  int32_t s_q, s_k;
+  int32_t causal, window;
+  int32_t out_bf16;
+  float scale;          // softmax scale sigma
+  float scale_log2;     // sigma * log2(e)
+  EpiArgs epi;
+};
+
+struct DecodeArgs {
+  const void* q;        // [bh_q, d]
+  const int8_t* k;      // [bh_kv, s_k, d]
+  const int8_t* v;
+  const float* k_scale; // [bh_kv, s_k]
+  const float* v_scale;
+  void* out;            // [bh_q, d]
+  float* lse;           // [bh_q] or null
+  float* partial;       // workspace [bh_q, num_splits, d + 2]
+  int32_t bh_q, bh_kv, group;
+  int32_t s_k;
+  int32_t key_lo;       // first visible key (window), 0 otherwise
+  int32_t num_splits;
+  int32_t tiles_per_split;
+  int32_t q_bf16, out_bf16;
+  float scale, scale_log2;
+  EpiArgs epi;
+};
+
+// Launchers return hipSuccess or the launch error; *name receives the instantiation name.
+hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d,
+                           int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int32_t d, int32_t kv_dtype, hipStream_t stream,
+                              const char** name);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, int32_t kv_dtype, hipStream_t stream,
+                               const char** name);
+hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, const char** name);
+
+}  // namespace fa
