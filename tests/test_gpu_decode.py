@@ -14,7 +14,7 @@ def _cache(k, v):
     kc, ks = fa.compress_kv(to_dev(k, "f32"))
     vc, vs = fa.compress_kv(to_dev(v, "f32"))
     host = (to_np(kc).astype(np.int8), to_np(ks), to_np(vc).astype(np.int8), to_np(vs))
-    return (kc, ks, vc, vs), host
+    return (kc, vc, ks, vs), host
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8, 6])
@@ -79,7 +79,7 @@ def test_decode_equals_last_row_of_fp32_prefill_on_the_same_cache():
     q = round_bf16(q)
     dev, _ = _cache(k, v)
     od = fa.decode(to_dev(q, "bf16"), *dev)
-    kc, ks, vc, vs = dev
+    kc, vc, ks, vs = dev
     op = fa.flash_attention(to_dev(q, "f32"), kc, vc, k_scale=ks, v_scale=vs, causal=True)
     check_close(to_np(od), to_np(op).astype(np.float64), 2e-6, "decode vs s_q = 1 prefill")
 
