@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X: prefill TFLOP/s against the bf16 MFMA peak and int8-KV
+decode GB/s against the HBM peak.
+
+Legs (each timed separately with HIP events on the stream the kernels run on):
+  c5     GQA causal prefill, bf16, batch 1, 64 query / 8 KV heads, 32768 tokens, d 128  <- `value`
+  c5w    the same with a 4096-token sliding window
+  c3     int8-KV causal prefill, bf16 Q, 4 x 32 heads, 4096 tokens, d 128, bf16 output
+  c4     GQA split-KV decode over the int8 cache, 16 x 32 query / 8 KV heads, 32768 keys, d 128
+  comp   per-token compression of the c4 K and V caches (fp32 -> int8 + fp32 scales)
+
+One JSON line on stdout; progress on stderr.  `--gpus N` with N > 1 exits: this path runs on one
+GPU (a multi-GPU run would shard KV heads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill attn TFLOP/s (% MFMA peak); int8-KV decode GB/s (% HBM peak)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(s_q, s_k, causal, window):
+    i = np.arange(s_q, dtype=np.int64) + (s_k - s_q)
+    hi = np.minimum(i + 1, s_k) if causal else np.full(s_q, s_k, np.int64)
+    lo = np.maximum(i - window + 1, 0) if window else np.zeros(s_q, np.int64)
+    return int(np.clip(hi - lo, 0, None).sum())
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int8_compressed_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, sha):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if taken on this source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(kernel)
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+class Timer:
+    """HIP events around each call on the current stream; returns per-call milliseconds."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup, flush=None):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            if flush is not None:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in times]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); this build has no "
+              "multi-GPU path: the kernels would run unchanged on each GPU's share of KV heads.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_compressed_kv_amd as fa
+    from synth_inputs import WORKLOADS, draw_qkv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    legs = set(args.legs.split(","))
+    timer = Timer(torch)
+    res = {}
+    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device="cuda")   # 2 GiB > MALL
+
+    def flush():
+        flush_buf.zero_()
+
+    def bf16_dev(x):
+        return torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+
+    cpu = {}
+    # ------------------------------------------------------------------ prefill legs c5 / c5w
+    if legs & {"c5", "c5w"}:
+        w = WORKLOADS["c5"]
+        log(f"[bench] generating {w.name}")
+        q, k, v = draw_qkv(w)
+        qd, kd, vd = bf16_dev(q), bf16_dev(k), bf16_dev(v)
+        out = torch.empty_like(qd)
+        for name, window in (("c5", 0), ("c5w", 4096)):
+            if name not in legs:
+                continue
+            ww = WORKLOADS[name]
+            flops = 4.0 * w.d * visible_pairs(w.s_q, w.s_k, True, window) * w.bh_q
+            fn = lambda: fa.flash_attention(qd, kd, vd, causal=True, window=window, out=out)   # noqa: E731
+            log(f"[bench] timing {ww.name}")
+            ms = timer.run(fn, args.steps, args.warmup)
+            avg = float(np.mean(ms))
+            res[name] = {"workload": ww.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
+                         "flop_per_launch": flops, "tflops": flops / avg / 1e9,
+                         "frac_of_peak": flops / avg / 1e9 / PEAK_BF16_TFLOPS}
+            log(f"[bench] {name}: {avg:.3f} ms  {res[name]['tflops']:.1f} TFLOP/s")
+            if name == "c5" and not args.no_cpu:
+                cpu["c5"] = prefill_cpu_baseline(q, k, v, out, w, args.cpu_seconds)
+        del qd, kd, vd, out, q, k, v
+
+    # ------------------------------------------------------------------ int8-KV prefill c3
+    if "c3" in legs:
+        w = WORKLOADS["c3"]
+        log(f"[bench] generating {w.name}")
+        q, k, v = draw_qkv(w)
+        qd = bf16_dev(q)
+        kc, ks = fa.compress_kv(torch.from_numpy(k).cuda())
+        vc, vs = fa.compress_kv(torch.from_numpy(v).cuda())
+        out = torch.empty_like(qd)
+        flops = 4.0 * w.d * visible_pairs(w.s_q, w.s_k, True, 0) * w.bh_q
+        fn = lambda: fa.flash_attention(qd, kc, vc, k_scale=ks, v_scale=vs, causal=True, out=out)   # noqa: E731
+        log(f"[bench] timing {w.name}")
+        ms = timer.run(fn, args.steps, args.warmup)
+        avg = float(np.mean(ms))
+        res["c3"] = {"workload": w.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
+                     "flop_per_launch": flops, "tflops": flops / avg / 1e9,
+                     "frac_of_peak": flops / avg / 1e9 / PEAK_BF16_TFLOPS}
+        log(f"[bench] c3: {avg:.3f} ms  {res['c3']['tflops']:.1f} TFLOP/s")
+        del qd, kc, ks, vc, vs, out, q, k, v
+
+    # ------------------------------------------------------------------ compress + decode c4
+    if legs & {"c4", "comp"}:
+        w = WORKLOADS["c4"]
+        log(f"[bench] generating {w.name}")
+        q, k, v = draw_qkv(w)
+        qd = bf16_dev(q)
+        kf = torch.from_numpy(k).cuda()
+        vf = torch.from_numpy(v).cuda()
+        kc = torch.empty(kf.shape, dtype=torch.int8, device="cuda")
+        vc = torch.empty_like(kc)
+        ks = torch.empty(kf.shape[:-1], dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        n_tok = w.bh_kv * w.s_k
+        if "comp" in legs:
+            fn = lambda: fa.compress_kv(kf, kc, ks)   # noqa: E731
+            log("[bench] timing compress (c4 K cache)")
+            ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = n_tok * w.d * 4 + n_tok * w.d + n_tok * 4
+            res["comp"] = {"workload": "compress_c4_k_cache_128x32768x128_f32", "ms": avg, "ms_min": float(np.min(ms)),
+                           "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
+                           "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] comp: {avg:.3f} ms  {res['comp']['gbs']:.0f} GB/s")
+        fa.compress_kv(kf, kc, ks)
+        fa.compress_kv(vf, vc, vs)
+        del kf, vf
+        out = torch.empty((w.bh_q, 1, w.d), dtype=torch.float32, device="cuda")
+        splits = fa.decode_num_splits(w.bh_q, w.bh_kv, w.s_k, w.d)
+        ws = torch.empty(fa.decode_workspace_bytes(w.bh_q, w.bh_kv, w.s_k, w.d, splits), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: fa.decode(qd, kc, vc, ks, vs, num_splits=splits, out=out, workspace=ws)   # noqa: E731
+        if "c4" in legs:
+            log(f"[bench] timing {w.name}")
+            ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = (2 * w.bh_kv * w.s_k * w.d + 2 * w.bh_kv * w.s_k * 4 + w.bh_q * w.d * 2 + w.bh_q * w.d * 4)
+            res["c4"] = {"workload": w.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
+                         "num_splits": splits, "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
+                         "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] c4: {avg * 1e3:.1f} us  {res['c4']['gbs']:.0f} GB/s")
+            if not args.no_cpu:
+                cpu["c4"] = decode_cpu_baseline(q, kc, ks, vc, vs, out, w, args.cpu_seconds)
+        del qd, kc, vc, ks, vs, out, ws
+
+    line = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": WORKLOADS["c5"].name, "batch": 1, "heads_q": 64, "heads_kv": 8,
+                       "seq_len": 32768, "head_dim": 128, "causal": True, "parallelism": "single-gpu"}}
+    if "c5" in res:
+        r = res["c5"]
+        line["value"] = round(r["tflops"], 2)
+        line["ms_per_step"] = round(r["ms"], 4)
+        line["roofline"] = {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(r["frac_of_peak"], 4),
+                            "traffic": traffic_for("prefill_bf16", source_sha("prefill_bf16.hip", "device_common.hpp")),
+                            "kernel": r["kernel"], "flop_per_launch": r["flop_per_launch"]}
+    if "c4" in res:
+        r = res["c4"]
+        line["decode"] = {"metric": "int8-KV decode GB/s", "value": round(r["gbs"], 1), "unit": "GB/s",
+                          "ms": round(r["ms"], 5), "workload": r["workload"], "num_splits": r["num_splits"],
+                          "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": round(r["frac_of_peak"], 4),
+                                       "traffic": traffic_for("decode_partial", source_sha("decode.hip", "device_common.hpp")),
+                                       "bytes_per_launch": r["bytes_per_launch"]}}
+        if "c4" in cpu:
+            line["decode"]["cpu_baseline"] = cpu["c4"]
+    line["legs"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                    for k, r in res.items()}
+    if "c5" in cpu:
+        line["cpu_baseline"] = cpu["c5"]
+    print(json.dumps(line), flush=True)
+
+
+def prefill_cpu_baseline(q, k, v, out_gpu, w, budget_s):
+    """The oracle on the host cores over the last rows of query heads of the c5 workload (the rows
+    that see the most keys), for about `budget_s` seconds; also checks those rows of the GPU output."""
+    import oracle
+    import torch
+    G = w.group
+    rows_per = 256
+    t0 = time.perf_counter()
+    flops = 0.0
+    err = 0.0
+    done = []
+    h = 0
+    while time.perf_counter() - t0 < budget_s and h < w.bh_q:
+        rows = list(range(w.s_q - rows_per, w.s_q))
+        o, _ = oracle.attention(q[h:h + 1], k[h // G:h // G + 1], v[h // G:h // G + 1], causal=True, rows=rows)
+        flops += 4.0 * w.d * sum(min(i + 1, w.s_k) for i in rows)
+        g = out_gpu[h, rows[0]:rows[-1] + 1].float().cpu().numpy()
+        err = max(err, float(np.abs(g - o[0, rows]).max()))
+        done.append(h)
+        h += 1
+    dt = time.perf_counter() - t0
+    log(f"[bench] oracle c5 sample: {len(done)} heads x {rows_per} rows in {dt:.1f}s, gpu max err {err:.2e}")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, {len(done)} query heads x the last {rows_per} rows of {w.name} "
+                      f"({flops / 1e9:.1f} GFLOP, {dt:.1f} s)",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "gpu_max_abs_err_on_sample": err}
+
+
+def decode_cpu_baseline(q, kc, ks, vc, vs, out_gpu, w, budget_s):
+    """The oracle decode over whole KV heads of the c4 cache for about `budget_s` seconds; the bytes
+    it covers are counted like the GPU leg's (codes, scales, Q, output)."""
+    import oracle
+    G = w.group
+    wall0 = time.perf_counter()
+    t_oracle = 0.0
+    nbytes = 0
+    err = 0.0
+    kvh = 0
+    og = out_gpu.cpu().numpy()
+    while time.perf_counter() - wall0 < budget_s and kvh < w.bh_kv:
+        kq = kc[kvh:kvh + 1].cpu().numpy()
+        vq = vc[kvh:kvh + 1].cpu().numpy()
+        ksh = ks[kvh:kvh + 1].cpu().numpy()
+        vsh = vs[kvh:kvh + 1].cpu().numpy()
+        t1 = time.perf_counter()
+        o, _ = oracle.decode(q[kvh * G:(kvh + 1) * G], kq, vq, k_scale=ksh, v_scale=vsh)
+        t_oracle += time.perf_counter() - t1
+        err = max(err, float(np.abs(og[kvh * G:(kvh + 1) * G] - o).max()))
+        nbytes += 2 * w.s_k * w.d + 2 * w.s_k * 4 + G * w.d * 6
+        kvh += 1
+    dt = t_oracle
+    log(f"[bench] oracle c4 sample: {kvh} KV heads in {dt:.1f}s, gpu max err {err:.2e}")
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode, {kvh} of {w.bh_kv} KV heads of {w.name}",
+            "seconds": round(dt, 2), "gpu_max_abs_err_on_sample": err}
+
+
+if __name__ == "__main__":
+    main()

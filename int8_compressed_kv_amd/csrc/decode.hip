@@ -377,23 +377,27 @@ __global__ __launch_bounds__(256, 2) void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// Pass 2: one wave per query head merges the splits' partial states.
+// Pass 2: one single-wave workgroup per query head merges the splits' partial states; the
+// split loop is unrolled so the partial-state loads of several splits are in flight together.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = (D + 63) / 64;
-  const int lane = threadIdx.x & 63;
-  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (head >= a.bh_q) return;
+  const int lane = threadIdx.x;
+  const int head = blockIdx.x;
   const float c2 = a.scale_log2;
-  const float* p = a.partial + (int64_t)head * a.num_splits * (D + 2);
+  const int S = a.num_splits;
+  const float* p = a.partial + (int64_t)head * S * (D + 2);
   float M = neg_inf();
-  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
   float L = 0.f;
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
   if (M != neg_inf()) {
-    for (int s = 0; s < a.num_splits; ++s) {
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) {
       const float* ps = p + (int64_t)s * (D + 2);
       const float w = __builtin_amdgcn_exp2f((ps[0] - M) * c2);
       L += w * ps[1];
@@ -405,13 +409,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
   }
   const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
+  float y[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) y[e] = o[e] * inv;
+  apply_epilogue_all(y, a.epi);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int d = lane + 64 * e;
     if (d < D) {
-      const float y = apply_epilogue(o[e] * inv, a.epi);
-      if (a.out_bf16) static_cast<__bf16*>(a.out)[(int64_t)head * D + d] = (__bf16)y;
-      else static_cast<float*>(a.out)[(int64_t)head * D + d] = y;
+      if (a.out_bf16) static_cast<__bf16*>(a.out)[(int64_t)head * D + d] = (__bf16)y[e];
+      else static_cast<float*>(a.out)[(int64_t)head * D + d] = y[e];
     }
   }
   if (a.lse && lane == 0) a.lse[head] = L > 0.f ? M * a.scale + logf(L) : neg_inf();
@@ -426,7 +433,7 @@ hipError_t launch_dct(const DecodeArgs& a_in, hipStream_t st) {
   hipLaunchKernelGGL((decode_partial_kernel<D, CT>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((a.bh_q + 3) / 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.bh_q), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -110,6 +110,21 @@ __device__ __forceinline__ float apply_epilogue(float x, const EpiArgs& e) {
   return x;
 }
 
+// The same ops over an array, op-major: one uniform branch per op.
+template <int N>
+__device__ __forceinline__ void apply_epilogue_all(float (&x)[N], const EpiArgs& e) {
+  for (int i = 0; i < e.n; ++i) {
+    const float cv = e.value[i];
+    if (e.kind[i] == kEpiMul) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) x[j] = __fmul_rn(x[j], cv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < N; ++j) x[j] = __fadd_rn(x[j], cv);
+    }
+  }
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
 }  // namespace fa

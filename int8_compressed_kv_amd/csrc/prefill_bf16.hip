@@ -10,45 +10,56 @@
 // Finally O / l, the epilogue ops in fp32, and the store.
 //
 // gfx950 mapping
-//   * One workgroup = 4 waves; each wave owns 32*QB query rows (QB = 2 for head_dim <= 128)
-//     and keeps its Q fragments in registers for the whole kernel.
-//   * K and V tiles of 64 keys are staged through LDS with double buffering: the global loads
-//     of tile t+1 are issued before the MFMAs of tile t and written to LDS after them, one
-//     barrier per tile.  V is transposed on the way into LDS (keys contiguous per head-dim
-//     row) so the P.V operand is two 8-byte LDS reads per lane.
-//   * The transposed product S^T = K Q^T (keys = MFMA rows, queries = columns) puts each
-//     query's scores in one lane pair; the row max needs one exchange between the pair, and
-//     P^T in the MFMA accumulator layout is already the B operand of O^T += V^T P^T.
-//   * The running max is only raised when a row's tile max exceeds it by more than 2^8 (in
-//     the exp2 domain); otherwise the stale max is kept, which leaves O and l mutually
-//     consistent and skips the O rescale.  P then stays below 2^8.
-//   * int8 K/V: codes are converted exactly to bf16 (K) and fp16 (V) while staging into LDS
-//     (the compressed cache is never expanded in global memory).  The per-token scale k_s is
-//     applied to S in registers; v_s is folded into P, which is rounded to fp16 for the fp16
-//     MFMA, after a power-of-two normalisation (2^-E, E from the largest v_s the block
-//     visits) that keeps P * v_s inside fp16 range; O is multiplied back by 2^E at the end.
-//   * Tiles wholly outside a wave's causal / window band are skipped; per-element masks are
-//     applied only on boundary tiles.  Blocks are ordered longest-first for causal masks and
+//   * A workgroup is 8 waves = 256 query rows (4 waves for head_dim > 128, whose fragments
+//     need the whole register file); each wave owns 32 rows and keeps their Q fragments in
+//     registers.  Two waves per SIMD: while one runs the softmax on the vector ALU the other
+//     keeps the matrix core busy.
+//   * K and V tiles of 64 keys live in LDS row-major, 16-byte chunks XOR-swizzled by row so
+//     that both operand reads below are free of bank conflicts.  Tiles are double-buffered:
+//     the global loads of tile t+1 are in flight (in registers) while tile t is computed, then
+//     written to the other LDS stage; one barrier per tile.
+//   * S^T = K Q^T (keys = MFMA rows, queries = columns) on v_mfma_f32_32x32x16_bf16: each
+//     query's scores sit in one lane pair, so the row max needs one exchange, and P^T in the
+//     accumulator layout is already the B operand of O^T += V^T P^T.  The V^T operand (8 keys
+//     of one head-dim column per lane) comes from two transposing LDS reads
+//     (ds_read_b64_tr_b16) of the row-major tile.
+//   * The running max is only raised when a row's tile max exceeds it by more than 2^8 in the
+//     exp2 domain; otherwise the stale max is kept (O and l stay mutually consistent, the O
+//     rescale is skipped) and P stays below 2^8.
+//   * int8 K/V: codes are converted exactly to bf16 (K) and fp16 (V) on their way from the
+//     staging registers into LDS -- the compressed cache is never expanded in global memory.  k_s
+//     scales S in registers; v_s is folded into P, rounded to fp16 for the fp16 MFMA, after a
+//     power-of-two normalisation 2^-E (E from the largest v_s the block visits) that keeps
+//     P * v_s in fp16 range; O is multiplied back by 2^E at the end.
+//   * Tiles wholly outside a wave's causal / window band are skipped; element masks are
+//     applied only on boundary tiles.  Blocks run longest-first under causal masks and are
 //     dealt to the 8 XCDs so that the G query heads sharing a KV head stay on one XCD.
 #include "device_common.hpp"
 
 namespace fa {
 namespace {
 
+typedef short s16x4v __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
+
 template <int D>
 struct Cfg {
-  static constexpr int QB = D <= 128 ? 2 : 1;   // 32-row query blocks per wave
-  static constexpr int NW = 4;                  // waves per workgroup
-  static constexpr int BM = NW * 32 * QB;       // query rows per workgroup
-  static constexpr int BN = 64;                 // keys per tile
-  static constexpr int KST = D + 8;             // K row stride in LDS (16-bit elements)
-  static constexpr int VST = BN + 4;            // V^T row stride in LDS (16-bit elements)
-  static constexpr int K_ELEMS = BN * KST;
-  static constexpr int V_ELEMS = D * VST;
-  static constexpr int KCH = D / 32;            // K 8-element chunks per thread per tile
-  static constexpr int VGRP = (2 * D + 255) / 256;  // V 4x8 groups per thread per tile
-  static constexpr float kLazyLog2 = 8.0f;      // stale-max headroom, exp2 domain
+  static constexpr int NW = D <= 128 ? 8 : 4;    // waves per workgroup (2 or 1 per SIMD)
+  static constexpr int BM = 32 * NW;             // query rows per workgroup
+  static constexpr int BN = 64;                  // keys per LDS tile
+  static constexpr int NC = D / 8;               // 16-byte chunks per row
+  static constexpr int TILE = BN * D;            // 16-bit elements per K or V tile
+  static constexpr int SWZ = (NC % 16 == 0) ? 16 : (NC % 8 == 0) ? 8 : 4;   // swizzle span
+  static constexpr int CH = (BN * NC + 64 * NW - 1) / (64 * NW);   // chunks per thread per matrix
+  static constexpr float kLazyLog2 = 8.0f;       // stale-max headroom, exp2 domain
 };
+
+// chunk permutation of row r: rows r..r+3 land in disjoint 4-chunk groups, 16 rows in 16
+// distinct chunks.
+template <int SWZ>
+__device__ __forceinline__ int swz(int r) {
+  return (((r & 3) << 2) | ((r >> 2) & 3)) & (SWZ - 1);
+}
 
 __device__ __forceinline__ unsigned gather_byte(unsigned w0, unsigned w1, unsigned w2, unsigned w3, int b) {
   const unsigned s = 8u * b;
@@ -57,23 +68,26 @@ __device__ __forceinline__ unsigned gather_byte(unsigned w0, unsigned w1, unsign
 }
 
 template <int D, bool KV_I8>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(PrefillArgs a) {
   using C = Cfg<D>;
-  constexpr int QB = C::QB, BM = C::BM, BN = C::BN, KST = C::KST, VST = C::VST;
+  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, NST = 2, CH = C::CH;
+  constexpr int SWZ = C::SWZ;
   constexpr int NKS = D / 16;   // 16-deep k-steps of Q.K
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O
 
-  __shared__ __attribute__((aligned(16))) unsigned short lds_k[2][C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) unsigned short lds_v[2][C::V_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lds_ks[2][KV_I8 ? BN : 1];
-  __shared__ __attribute__((aligned(16))) float lds_vs[2][KV_I8 ? BN : 1];
-  __shared__ float lds_red[4];
+  __shared__ __attribute__((aligned(16))) unsigned short lds_k[NST][C::TILE];
+  __shared__ __attribute__((aligned(16))) unsigned short lds_v[NST][C::TILE];
+  __shared__ __attribute__((aligned(16))) float lds_ks[NST][KV_I8 ? BN : 1];
+  __shared__ __attribute__((aligned(16))) float lds_vs[NST][KV_I8 ? BN : 1];
+  __shared__ float lds_red[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int c = lane & 31;
+  const int h = lane >> 5;       // half of the wave (MFMA k-slot group)
+  const int c = lane & 31;       // MFMA column (query) / row (key, head-dim)
+  const int g16 = lane >> 4;     // 16-lane group of the transposing reads
+  const int i16 = lane & 15;
 
   // ---- block -> (query block, head): longest-first, KV groups kept on one XCD
   const int G = a.group;
@@ -105,87 +119,71 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
   if (a.window) lo = max(0, q0 + off - a.window + 1);
   const int t_lo = lo / BN;
   const int n_tiles = hi > lo ? (hi + BN - 1) / BN - t_lo : 0;
-
   const int64_t kv_base = (int64_t)kvh * a.s_k;
 
   // ---- int8: power-of-two normalisation for P * v_s (largest v_s over [lo, hi))
   float vs_norm = 1.f, vs_unnorm = 1.f;
-  if (KV_I8) {
+  if constexpr (KV_I8) {
     float mx = 0.f;
-    for (int j = lo + tid; j < hi; j += 256) mx = fmaxf(mx, a.v_scale[kv_base + j]);
+    for (int j = lo + tid; j < hi; j += 64 * NW) mx = fmaxf(mx, a.v_scale[kv_base + j]);
 #pragma unroll
     for (int o2 = 32; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
     if (lane == 0) lds_red[wave] = mx;
     __syncthreads();
-    mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
+    mx = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_red[w]);
     int e = 0;
     if (mx > 0.f) (void)frexpf(mx, &e);   // mx = f * 2^e, f in [0.5, 1)
     vs_norm = ldexpf(1.f, -e);
     vs_unnorm = ldexpf(1.f, e);
   }
 
-  // ---- Q fragments: Qf[qb][ks] = Q[row][16 ks + 8 h .. + 8], row = q0 + 32 QB wave + 32 qb + c
-  const int qw0 = q0 + 32 * QB * wave;
+  // ---- Q fragments (B operand of S^T): Qf[ks] = Q[qw0 + c][16 ks + 8 h .. + 8]
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + c;
   const unsigned short* qp = static_cast<const unsigned short*>(a.q) + (int64_t)head * a.s_q * D;
-  bf16x8 Qf[QB][NKS];
+  bf16x8 Qf[NKS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + 32 * qb + c;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row < a.s_q) w = *reinterpret_cast<const u32x4*>(qp + (int64_t)row * D + 16 * ks + 8 * h);
-      Qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
-    }
+  for (int ks = 0; ks < NKS; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qi < a.s_q) w = *reinterpret_cast<const u32x4*>(qp + (int64_t)qi * D + 16 * ks + 8 * h);
+    Qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // ---- staging registers and helpers
   const unsigned short* kp16 = static_cast<const unsigned short*>(a.k) + kv_base * D;
   const unsigned short* vp16 = static_cast<const unsigned short*>(a.v) + kv_base * D;
   const int8_t* kp8 = static_cast<const int8_t*>(a.k) + kv_base * D;
   const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
+  const int last_key = a.s_k - 1;
 
-  u32x4 kreg[C::KCH];           // bf16: 8 elements; int8: 8 codes in [0..1]
-  u32x4 vreg[C::VGRP][4];       // bf16: 4 keys x 8 elements; int8: 4 keys x 8 codes in [0..1]
-  float sreg = 0.f;             // int8: one scale value per thread (threads < 128)
-
+  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks (8 bytes for int8 codes),
+  // double-buffered in registers, and written to LDS at row r, physical chunk lc ^ swz(r).
+  // int8 codes are converted exactly (K -> bf16, V -> fp16) on the way.
+  u32x4 kreg[CH], vreg[CH];
+  float sreg = 0.f;
   auto load_tile = [&](int t) {
     const int k0 = (t_lo + t) * BN;
 #pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int idx = tid + 256 * u;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (k0 + r < a.s_k) {
-        if (KV_I8) {
-          const u32x2 w2 = *reinterpret_cast<const u32x2*>(kp8 + (int64_t)(k0 + r) * D + 8 * c8);
-          w[0] = w2[0];
-          w[1] = w2[1];
+    for (int u = 0; u < CH; ++u) {
+      const int idx = tid + 64 * NW * u;
+      const int r = idx / NC, lc = idx % NC;
+      u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
+      if ((BN * NC % (64 * NW) == 0 || idx < BN * NC) && k0 + r < a.s_k) {
+        if constexpr (KV_I8) {
+          const u32x2 k2 = *reinterpret_cast<const u32x2*>(kp8 + (int64_t)(k0 + r) * D + 8 * lc);
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(vp8 + (int64_t)(k0 + r) * D + 8 * lc);
+          wk[0] = k2[0];
+          wk[1] = k2[1];
+          wv[0] = v2[0];
+          wv[1] = v2[1];
         } else {
-          w = *reinterpret_cast<const u32x4*>(kp16 + (int64_t)(k0 + r) * D + 8 * c8);
+          wk = *reinterpret_cast<const u32x4*>(kp16 + (int64_t)(k0 + r) * D + 8 * lc);
+          wv = *reinterpret_cast<const u32x4*>(vp16 + (int64_t)(k0 + r) * D + 8 * lc);
         }
       }
-      kreg[u] = w;
-    }
-#pragma unroll
-    for (int u = 0; u < C::VGRP; ++u) {
-      const int grp = tid + 256 * u;
-      const int kq = grp / (D / 8), dc = grp % (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = k0 + 4 * kq + r;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (grp < 2 * D && j < a.s_k) {
-          if (KV_I8) {
-            const u32x2 w2 = *reinterpret_cast<const u32x2*>(vp8 + (int64_t)j * D + 8 * dc);
-            w[0] = w2[0];
-            w[1] = w2[1];
-          } else {
-            w = *reinterpret_cast<const u32x4*>(vp16 + (int64_t)j * D + 8 * dc);
-          }
-        }
-        vreg[u][r] = w;
-      }
+      kreg[u] = wk;
+      vreg[u] = wv;
     }
     if (KV_I8 && tid < 2 * BN) {
       const int j = k0 + (tid % BN);
@@ -193,81 +191,43 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
       if (j < a.s_k) sreg = tid < BN ? a.k_scale[kv_base + j] : a.v_scale[kv_base + j] * vs_norm;
     }
   };
-
-  auto store_tile = [&](int stage) {
-    unsigned short* ks_ = lds_k[stage];
-    unsigned short* vs_ = lds_v[stage];
+  auto store_tile = [&](int st) {
 #pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int idx = tid + 256 * u;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      u32x4 w = kreg[u];
-      if (KV_I8) {
-        const u32x2 lo2 = i8x4_to_bf16x4(w[0]);
-        const u32x2 hi2 = i8x4_to_bf16x4(w[1]);
-        w[0] = lo2[0];
-        w[1] = lo2[1];
-        w[2] = hi2[0];
-        w[3] = hi2[1];
-      }
-      *reinterpret_cast<u32x4*>(ks_ + r * KST + 8 * c8) = w;
-    }
-#pragma unroll
-    for (int u = 0; u < C::VGRP; ++u) {
-      const int grp = tid + 256 * u;
-      if (grp < 2 * D) {
-        const int kq = grp / (D / 8), dc = grp % (D / 8);
-        if (KV_I8) {
-          // 4 keys x 8 codes -> for each of the 8 head-dim rows, 4 keys as fp16
-#pragma unroll
-          for (int dd = 0; dd < 8; ++dd) {
-            const int e = dd / 4, bb = dd % 4;
-            const unsigned k4 = gather_byte(vreg[u][0][e], vreg[u][1][e], vreg[u][2][e], vreg[u][3][e], bb);
-            const u32x2 f = i8x4_to_f16x4(k4);
-            *reinterpret_cast<u32x2*>(vs_ + (8 * dc + dd) * VST + 4 * kq) = f;
-          }
-        } else {
-          // 4 keys x 8 bf16 -> for each of the 8 head-dim rows, 4 keys (2 dwords)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned w0 = vreg[u][0][e], w1 = vreg[u][1][e], w2 = vreg[u][2][e], w3 = vreg[u][3][e];
-            u32x2 lo_d, hi_d;
-            lo_d[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-            lo_d[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-            hi_d[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-            hi_d[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-            *reinterpret_cast<u32x2*>(vs_ + (8 * dc + 2 * e) * VST + 4 * kq) = lo_d;
-            *reinterpret_cast<u32x2*>(vs_ + (8 * dc + 2 * e + 1) * VST + 4 * kq) = hi_d;
-          }
+    for (int u = 0; u < CH; ++u) {
+      const int idx = tid + 64 * NW * u;
+      if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
+        const int r = idx / NC, lc = idx % NC;
+        const int pc = lc ^ swz<SWZ>(r);
+        u32x4 kw = kreg[u], vw = vreg[u];
+        if constexpr (KV_I8) {
+          const u32x2 k0v = i8x4_to_bf16x4(kreg[u][0]), k1v = i8x4_to_bf16x4(kreg[u][1]);
+          const u32x2 v0v = i8x4_to_f16x4(vreg[u][0]), v1v = i8x4_to_f16x4(vreg[u][1]);
+          kw = u32x4{k0v[0], k0v[1], k1v[0], k1v[1]};
+          vw = u32x4{v0v[0], v0v[1], v1v[0], v1v[1]};
         }
+        *reinterpret_cast<u32x4*>(lds_k[st] + r * D + 8 * pc) = kw;
+        *reinterpret_cast<u32x4*>(lds_v[st] + r * D + 8 * pc) = vw;
       }
     }
     if (KV_I8 && tid < 2 * BN) {
-      if (tid < BN) lds_ks[stage][tid] = sreg;
-      else lds_vs[stage][tid - BN] = sreg;
+      if (tid < BN) lds_ks[st][tid] = sreg;
+      else lds_vs[st][tid - BN] = sreg;
     }
   };
 
   // ---- per-wave state
-  f32x16 O[QB][NDB];
+  f32x16 O[NDB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) O[qb][db][i] = 0.f;
-  float m_run[QB], l_run[QB], mc[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = neg_inf();
-    l_run[qb] = 0.f;
-    mc[qb] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+  float m_run = neg_inf(), l_run = 0.f, mc = 0.f;
   const float c2 = a.scale_log2;
   const float lazy_thr = C::kLazyLog2 / c2;   // raw-score headroom before the max is raised
-  const int w_last = qw0 + 32 * QB - 1;       // last query row of this wave (may be padding)
+  const int w_last = qw0 + 31;
   const bool wave_live = qw0 < a.s_q;
 
+  // ---- pipeline: the global loads of tile t+1 are in flight while tile t is computed
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
@@ -275,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
+    const int st = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
 
     const int k0 = (t_lo + t) * BN;
@@ -285,158 +245,149 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(PrefillArgs a) {
     if (!skip) {
       const bool need_mask = (k0 + BN > a.s_k) || (a.causal && k0 + BN - 1 > qw0 + off) ||
                              (a.window && k0 <= w_last + off - a.window);
-      const unsigned short* Kt = lds_k[stage];
-      const unsigned short* Vt = lds_v[stage];
+      const unsigned short* Kt = lds_k[st];
+      const unsigned short* Vt = lds_v[st];
 
-      // Two 32-key softmax steps per 64-key LDS tile (bounds the live score registers).
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T[qb]: key 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative), query 32 qb + c
-        f32x16 S[QB];
+        // S^T: lane holds keys 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative) for query qi
+        bf16x8 kf[NKS];
+        const int krow = 32 * kb + c;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int ks = 0; ks < NKS; ++ks)
+          kf[ks] = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
+        f32x16 S;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) S[qb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) S[i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kt + (32 * kb + c) * KST + 16 * ks + 8 * h);
+        for (int ks = 0; ks < NKS; ++ks) S = mfma32_bf16(kf[ks], Qf[ks], S);
+
+        // V^T fragments for this 32-key step: vf[s2][db] holds keys kbase + 0..3 and
+        // kbase + 8 + 0..3 (kbase = 32 kb + 16 s2 + 4 h) of head-dim 32 db + c
+        u32x4 vf[2][NDB];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) S[qb] = mfma32_bf16(ka, Qf[qb][ks], S[qb]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+            const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
+            const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
+            const s16x4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0));
+            const s16x4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+            vf[s2][db] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+          }
         }
-        if (KV_I8) {
+
+        if constexpr (KV_I8) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[stage][32 * kb + 8 * g4 + 4 * h]);
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[st][32 * kb + 8 * g4 + 4 * h]);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) S[qb][4 * g4 + e] *= sc[e];
+            for (int e = 0; e < 4; ++e) S[4 * g4 + e] *= sc[e];
           }
         }
         if (need_mask) {
+          // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
+          const int kl0 = k0 + 32 * kb + 4 * h;
+          int hi_i = a.s_k - 1 - kl0;
+          if (a.causal) hi_i = min(hi_i, qi + off - kl0);
+          int lo_i = a.window ? qi + off - a.window + 1 - kl0 : -0x40000000;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int qi = qw0 + 32 * qb + c;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = k0 + 32 * kb + 8 * (i / 4) + 4 * h + (i % 4);
-              bool vis = j < a.s_k;
-              if (a.causal) vis = vis && (j <= qi + off);
-              if (a.window) vis = vis && (j > qi + off - a.window);
-              if (!vis) S[qb][i] = neg_inf();
-            }
+          for (int i = 0; i < 16; ++i) {
+            const int ko = 8 * (i / 4) + (i % 4);
+            if (ko > hi_i || ko < lo_i) S[i] = neg_inf();
           }
         }
 
         // online softmax with a lazily raised max
-        float tmax[QB];
-        bool raise = false;
+        float mx = neg_inf();
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float mx = neg_inf();
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+        mx = fmaxf(mx, xor32(mx));
+        if (__any(mx - m_run > lazy_thr)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+          l_run *= alpha;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-          mx = fmaxf(mx, xor32(mx));
-          tmax[qb] = mx;
-          raise = raise || (mx - m_run[qb] > lazy_thr);
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+          m_run = m_new;
+          mc = m_use * c2;
         }
-        if (__any(raise)) {
+        float p[16];
+        float ps = 0.f;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const float m_new = fmaxf(m_run[qb], tmax[qb]);
-            const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_use) * c2);
-            l_run[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) O[qb][db][i] *= alpha;
-            m_run[qb] = m_new;
-            mc[qb] = m_use * c2;
-          }
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -mc));
+          ps += p[i];
         }
-
-        // P^T as B operands: k-step s2 (0, 1) covers keys 32 kb + 16 s2 + 8 (i/4) + 4 h + i%4
-        u32x4 Pw[QB][2];
+        l_run += ps;
+        // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7]
+        u32x4 Pw[2];
+        if constexpr (KV_I8) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float p[16];
-          float ps = 0.f;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[st][32 * kb + 8 * g4 + 4 * h]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][i], c2, -mc[qb]));
-            ps += p[i];
+            for (int e = 0; e < 4; ++e) p[4 * g4 + e] *= sc[e];
           }
-          l_run[qb] += ps;
-          if (KV_I8) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[stage][32 * kb + 8 * g4 + 4 * h]);
+          for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_f16x2(p[2 * q2], p[2 * q2 + 1]);
+        } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) p[4 * g4 + e] *= sc[e];
-            }
-#pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) Pw[qb][q2 / 4][q2 % 4] = pack_f16x2(p[2 * q2], p[2 * q2 + 1]);
-          } else {
-#pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) Pw[qb][q2 / 4][q2 % 4] = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
-          }
+          for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
         }
 
-        // O^T[qb][db] += V^T P^T
+        // O^T[db] += V^T P^T
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int kbase = 32 * kb + 16 * s2 + 4 * h;
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const unsigned short* vrow = Vt + (32 * db + c) * VST + kbase;
-            const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow);
-            const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 8);
-            const u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              if (KV_I8)
-                O[qb][db] = mfma32_f16(__builtin_bit_cast(f16x8, vw), __builtin_bit_cast(f16x8, Pw[qb][s2]), O[qb][db]);
-              else
-                O[qb][db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vw), __builtin_bit_cast(bf16x8, Pw[qb][s2]), O[qb][db]);
-            }
+            if constexpr (KV_I8)
+              O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf[s2][db]), __builtin_bit_cast(f16x8, Pw[s2]), O[db]);
+            else
+              O[db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf[s2][db]), __builtin_bit_cast(bf16x8, Pw[s2]), O[db]);
           }
-        }
       }
     }
 
-    if (t + 1 < n_tiles) store_tile(stage ^ 1);
+    if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
     __syncthreads();
   }
 
   // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
+  const float l_tot = l_run + xor32(l_run);
+  float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
+  if constexpr (KV_I8) inv *= vs_unnorm;
+  if (qi < a.s_q) {
+    float y[NDB * 16];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + xor32(l_run[qb]);
-    float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
-    if (KV_I8) inv *= vs_unnorm;
-    const int qi = qw0 + 32 * qb + c;
-    if (qi < a.s_q) {
-      const int64_t row = (int64_t)head * a.s_q + qi;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int i = 0; i < 16; ++i) y[16 * db + i] = O[db][i] * inv;
+    apply_epilogue_all(y, a.epi);
+    const int64_t row = (int64_t)head * a.s_q + qi;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * db + 8 * g4 + 4 * h;
-          float y[4];
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = apply_epilogue(O[qb][db][4 * g4 + e] * inv, a.epi);
-          if (a.out_bf16) {
-            u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-            *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + d0) = w;
-          } else {
-            f32x4 w = {y[0], y[1], y[2], y[3]};
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = w;
-          }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        const float* yy = y + 16 * db + 4 * g4;
+        if (a.out_bf16) {
+          const u32x2 w = {pack_bf16x2(yy[0], yy[1]), pack_bf16x2(yy[2], yy[3])};
+          *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + d0) = w;
+        } else {
+          const f32x4 w = {yy[0], yy[1], yy[2], yy[3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = w;
         }
       }
-      if (a.lse && h == 0) a.lse[row] = l_tot > 0.f ? m_run[qb] * a.scale + logf(l_tot) : neg_inf();
-    }
+    if (a.lse && h == 0) a.lse[row] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : neg_inf();
   }
 }
 
@@ -446,10 +397,10 @@ hipError_t launch_d(const PrefillArgs& a, int32_t kv_dtype, hipStream_t st, cons
   const int64_t blocks = n_qb * a.bh_q;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (kv_dtype == kI8) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
     *name = "prefill_bf16_i8kv";
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
     *name = "prefill_bf16";
   }
   return hipGetLastError();

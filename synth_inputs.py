@@ -62,9 +62,9 @@ WORKLOADS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even); return the uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite values stay below 0xFF800000, so the rounding increment cannot wrap in uint32
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
