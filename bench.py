@@ -8,6 +8,8 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   c3     int8-KV causal prefill, bf16 Q, 4 x 32 heads, 4096 tokens, d 128, bf16 output
   c4     GQA split-KV decode over the int8 cache, 16 x 32 query / 8 KV heads, 32768 keys, d 128
   comp   per-token compression of the c4 K and V caches (fp32 -> int8 + fp32 scales)
+  copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
+         that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to HBM bytes
 
 One JSON line on stdout; progress on stderr.  `--gpus N` with N > 1 exits: this path runs on one
 GPU (a multi-GPU run would shard KV heads).
@@ -215,6 +217,20 @@ def main():
             if not args.no_cpu:
                 cpu["c4"] = decode_cpu_baseline(q, kc, ks, vc, vs, out, w, args.cpu_seconds)
         del qd, kc, vc, ks, vs, out, ws
+
+    if "copy" in legs:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        fn = lambda: dst.copy_(src)   # noqa: E731
+        log("[bench] timing copy 1 GiB")
+        ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+        avg = float(np.mean(ms))
+        nbytes = 2 * src.numel() * 4
+        res["copy"] = {"workload": "device_copy_1GiB", "ms": avg, "bytes_per_launch": nbytes,
+                       "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+        log(f"[bench] copy: {avg:.3f} ms  {res['copy']['gbs']:.0f} GB/s")
+        del src, dst
 
     line = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",

@@ -64,7 +64,7 @@ float resolve_scale(float s, int32_t d) {
 }
 
 constexpr int32_t kMaxSplits = 4096;
-constexpr int32_t kDecodeTile = 64;   // keys per decode tile
+constexpr int32_t kDecodeTile = 32;   // keys per decode tile
 
 }  // namespace
 
@@ -166,9 +166,9 @@ int32_t fa_decode_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t h
   const int32_t col_groups = (group + 3) / 4;   // decode workgroups per (split, KV head)
   const int64_t units = (int64_t)bh_kv * col_groups;
   const int32_t tiles = (s_k + kDecodeTile - 1) / kDecodeTile;
-  // aim for ~2048 workgroups, with at least 8 tiles (512 keys) per split
-  int64_t splits = (2048 + units - 1) / units;
-  const int64_t max_by_len = tiles / 8 > 0 ? tiles / 8 : 1;
+  // one workgroup per CU (256), each split keeping at least 16 tiles (4 per wave)
+  int64_t splits = (256 + units - 1) / units;
+  const int64_t max_by_len = tiles / 16 > 0 ? tiles / 16 : 1;
   if (splits > max_by_len) splits = max_by_len;
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;
