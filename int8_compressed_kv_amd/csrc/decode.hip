@@ -10,9 +10,11 @@
 // O = sum O_s e^(m_s - M) / L, then the epilogue and the store.
 //
 // HBM-bound.  Every K/V byte is read once for all query heads of its group.  Each wave streams
-// its own tiles of 64 keys (32 for head_dim > 128) with plain 16-byte vector loads into a ring of register tiles (the
-// next NT - 1 tiles, 16 x 16 bytes per lane each, are in flight while the current one is
-// computed): on gfx950 this sustains a higher read rate than direct global -> LDS copies.  K is loaded
+// its own tiles of 32 keys with plain 16-byte vector loads into two register tiles (the next
+// tile is in flight while the current one is computed): on gfx950 this sustains a higher read
+// rate than direct global -> LDS copies.  All cache reads, the per-key scales included, are
+// nontemporal: ordinary cached loads of the small scale vectors interleaved with the streaming
+// code loads measurably lower the achieved read bandwidth.  K is loaded
 // straight into its MFMA operand layout; V passes through a small wave-private LDS slot so
 // that the transposing read can hand each lane 16 keys of one head-dim column.  No barriers
 // are needed until the final combine.
@@ -44,19 +46,13 @@ constexpr int kFlushTiles = 1024;   // int32 P~V accumulator bound: 1024 tiles x
 
 template <int D>
 struct DCfg {
-#ifndef FA_DECODE_KT
-#define FA_DECODE_KT 64
-#endif
-  static constexpr int KT = D <= 128 ? FA_DECODE_KT : 32;   // keys per tile
+  static constexpr int KT = 32;                           // keys per tile
   static constexpr int NC16 = D / 16;                     // 16-byte chunks per row
   static constexpr int SP = (NC16 % 8 == 0) ? 8 : (NC16 % 4 == 0) ? 4 : 2;   // swizzle span
   static constexpr int VCH = KT * NC16 / 64;              // 16-byte V loads per lane per tile
   static constexpr int NSC = 2 * KT / 64;                 // scale values per lane per tile
   static constexpr int SLOT = KT * D + 8 * KT;            // wave-private LDS bytes (V tile, scales)
-#ifndef FA_DECODE_NT
-#define FA_DECODE_NT 3
-#endif
-  static constexpr int NT = D <= 128 ? FA_DECODE_NT : 2;  // register tile buffers per wave
+  static constexpr int NT = 2;                            // register tile buffers per wave
 };
 
 template <int N>
@@ -226,7 +222,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     for (int e = 0; e < NSC; ++e) {
       const int slot_i = 64 * e + lane;            // < 2 KT
       const int r = min(slot_i % KT, lim);
-      T.sc[e] = slot_i < KT ? kst[r] : vst[r];
+      T.sc[e] = __builtin_nontemporal_load((slot_i < KT ? kst : vst) + r);
     }
   };
   unsigned char* slot = &lds_slot[wave][0];
