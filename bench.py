@@ -44,23 +44,35 @@ def visible_pairs(s_q, s_k, causal, window):
     return int(np.clip(hi - lo, 0, None).sum())
 
 
-def source_sha(*names):
+# kernel sources behind each leg: a counter reading is used only while these are unchanged
+LEG_SOURCES = {
+    "c5": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
+    "c5w": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
+    "c3": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
+    "c4": ("decode.hip", "device_common.hpp", "kernel_args.hpp"),
+    "comp": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
+}
+
+
+def source_sha(leg):
     h = hashlib.sha256()
-    for n in names:
+    for n in LEG_SOURCES[leg]:
         with open(os.path.join(ROOT, "int8_compressed_kv_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, sha):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if taken on this source."""
+def traffic_for(leg):
+    """HBM bytes per launch of the leg's kernels from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by the copy calibration), or None if they were taken on other kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
-    rec = json.load(open(p)).get(kernel)
-    if not rec or rec.get("source_sha") != sha:
+    with open(p) as f:
+        rec = json.load(f).get("legs", {}).get(leg)
+    if not rec or rec.get("source_sha") != source_sha(leg):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch")
 
 
 def blas_threads():
@@ -243,7 +255,7 @@ def main():
         line["ms_per_step"] = round(r["ms"], 4)
         line["roofline"] = {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(r["frac_of_peak"], 4),
-                            "traffic": traffic_for("prefill_bf16", source_sha("prefill_bf16.hip", "device_common.hpp")),
+                            "traffic": traffic_for("c5"),
                             "kernel": r["kernel"], "flop_per_launch": r["flop_per_launch"]}
     if "c4" in res:
         r = res["c4"]
@@ -251,10 +263,14 @@ def main():
                           "ms": round(r["ms"], 5), "workload": r["workload"], "num_splits": r["num_splits"],
                           "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": PEAK_HBM_GBS,
                                        "unit": "GB/s", "frac": round(r["frac_of_peak"], 4),
-                                       "traffic": traffic_for("decode_partial", source_sha("decode.hip", "device_common.hpp")),
+                                       "traffic": traffic_for("c4"),
                                        "bytes_per_launch": r["bytes_per_launch"]}}
         if "c4" in cpu:
             line["decode"]["cpu_baseline"] = cpu["c4"]
+    for k, r in res.items():
+        if k in LEG_SOURCES:
+            r["source_sha"] = source_sha(k)
+            r["traffic"] = traffic_for(k)
     line["legs"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
                     for k, r in res.items()}
     if "c5" in cpu:
