@@ -48,7 +48,7 @@ def visible_pairs(s_q, s_k, causal, window):
 LEG_SOURCES = {
     "c5": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
     "c5w": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
-    "c3": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
+    "c3": ("prefill_i8kv.hip", "device_common.hpp", "kernel_args.hpp"),
     "c4": ("decode.hip", "device_common.hpp", "kernel_args.hpp"),
     "comp": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
 }

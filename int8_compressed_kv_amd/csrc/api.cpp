@@ -152,8 +152,10 @@ int fa_forward(const void* q, int32_t q_dtype, const void* k, const void* v, int
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.epi = ea;
   const char* name = "";
-  hipError_t e = f32_path ? fa::launch_prefill_f32(a, head_dim, kv_dtype, static_cast<hipStream_t>(stream), &name)
-                          : fa::launch_prefill_bf16(a, head_dim, kv_dtype, static_cast<hipStream_t>(stream), &name);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = f32_path              ? fa::launch_prefill_f32(a, head_dim, kv_dtype, st, &name)
+                 : kv_dtype == FA_I8   ? fa::launch_prefill_i8kv(a, head_dim, st, &name)
+                                       : fa::launch_prefill_bf16(a, head_dim, st, &name);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   g_last_kernel = name;
   return FA_OK;

@@ -60,8 +60,8 @@ hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int
                            int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int32_t d, int32_t kv_dtype, hipStream_t stream,
                               const char** name);
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, int32_t kv_dtype, hipStream_t stream,
-                               const char** name);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
+hipError_t launch_prefill_i8kv(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, const char** name);
 
 }  // namespace fa

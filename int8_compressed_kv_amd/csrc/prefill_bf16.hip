@@ -1,9 +1,9 @@
-// bf16 attention forward on gfx950 MFMA, for bf16 Q with bf16 K/V or with the int8
-// per-token KV cache.
+// bf16 attention forward on gfx950 MFMA, for bf16 Q, K and V (the int8-cache variant of the
+// same kernel is prefill_i8kv.hip).
 //
 // Method: FlashAttention-2 style tiled forward with an online softmax (fkl.flash_attention
-// PR, Summary: FA-2 forward, fp32 accumulation, compressed int8 KV dequantized inside q.k and
-// p.v; Foundry attention/ README, References: the online-softmax recurrence).  For each key
+// PR, Summary: FA-2 forward, fp32 accumulation; Foundry attention/ README, References: the
+// online-softmax recurrence).  For each key
 // tile, with running row max m, running sum l and accumulator O:
 //   S = sigma * Q K^T (masked) ; m' = max(m, rowmax S) ; P = exp(S - m') ;
 //   l = exp(m - m') l + rowsum P ; O = exp(m - m') O + P V.
@@ -17,7 +17,8 @@
 //   * K and V tiles of 64 keys live in LDS row-major, 16-byte chunks XOR-swizzled by row so
 //     that both operand reads below are free of bank conflicts.  Tiles are double-buffered:
 //     the global loads of tile t+1 are in flight (in registers) while tile t is computed, then
-//     written to the other LDS stage; one barrier per tile.
+//     written to the other LDS stage; one barrier per tile.  For head_dim <= 128 the tile loop
+//     is unrolled by two so that the stage is a compile-time constant in every LDS address.
 //   * S^T = K Q^T (keys = MFMA rows, queries = columns) on v_mfma_f32_32x32x16_bf16: each
 //     query's scores sit in one lane pair, so the row max needs one exchange, and P^T in the
 //     accumulator layout is already the B operand of O^T += V^T P^T.  The V^T operand (8 keys
@@ -26,14 +27,11 @@
 //   * The running max is only raised when a row's tile max exceeds it by more than 2^8 in the
 //     exp2 domain; otherwise the stale max is kept (O and l stay mutually consistent, the O
 //     rescale is skipped) and P stays below 2^8.
-//   * int8 K/V: codes are converted exactly to bf16 (K) and fp16 (V) on their way from the
-//     staging registers into LDS -- the compressed cache is never expanded in global memory.  k_s
-//     scales S in registers; v_s is folded into P, rounded to fp16 for the fp16 MFMA, after a
-//     power-of-two normalisation 2^-E (E from the largest v_s the block visits) that keeps
-//     P * v_s in fp16 range; O is multiplied back by 2^E at the end.
 //   * Tiles wholly outside a wave's causal / window band are skipped; element masks are
 //     applied only on boundary tiles.  Blocks run longest-first under causal masks and are
 //     dealt to the 8 XCDs so that the G query heads sharing a KV head stay on one XCD.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace fa {
@@ -61,13 +59,7 @@ __device__ __forceinline__ int swz(int r) {
   return (((r & 3) << 2) | ((r >> 2) & 3)) & (SWZ - 1);
 }
 
-__device__ __forceinline__ unsigned gather_byte(unsigned w0, unsigned w1, unsigned w2, unsigned w3, int b) {
-  const unsigned s = 8u * b;
-  return ((w0 >> s) & 0xffu) | (((w1 >> s) & 0xffu) << 8) | (((w2 >> s) & 0xffu) << 16) |
-         (((w3 >> s) & 0xffu) << 24);
-}
-
-template <int D, bool KV_I8>
+template <int D>
 __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(PrefillArgs a) {
   using C = Cfg<D>;
   constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, NST = 2, CH = C::CH;
@@ -77,8 +69,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
 
   __shared__ __attribute__((aligned(16))) unsigned short lds_k[NST][C::TILE];
   __shared__ __attribute__((aligned(16))) unsigned short lds_v[NST][C::TILE];
-  __shared__ __attribute__((aligned(16))) float lds_ks[NST][KV_I8 ? BN : 1];
-  __shared__ __attribute__((aligned(16))) float lds_vs[NST][KV_I8 ? BN : 1];
   __shared__ float lds_red[NW];
 
   const int tid = threadIdx.x;
@@ -121,24 +111,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   const int n_tiles = hi > lo ? (hi + BN - 1) / BN - t_lo : 0;
   const int64_t kv_base = (int64_t)kvh * a.s_k;
 
-  // ---- int8: power-of-two normalisation for P * v_s (largest v_s over [lo, hi))
-  float vs_norm = 1.f, vs_unnorm = 1.f;
-  if constexpr (KV_I8) {
-    float mx = 0.f;
-    for (int j = lo + tid; j < hi; j += 64 * NW) mx = fmaxf(mx, a.v_scale[kv_base + j]);
-#pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
-    if (lane == 0) lds_red[wave] = mx;
-    __syncthreads();
-    mx = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_red[w]);
-    int e = 0;
-    if (mx > 0.f) (void)frexpf(mx, &e);   // mx = f * 2^e, f in [0.5, 1)
-    vs_norm = ldexpf(1.f, -e);
-    vs_unnorm = ldexpf(1.f, e);
-  }
-
   // ---- Q fragments (B operand of S^T): Qf[ks] = Q[qw0 + c][16 ks + 8 h .. + 8]
   const int qw0 = q0 + 32 * wave;
   const int qi = qw0 + c;
@@ -153,42 +125,22 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
 
   const unsigned short* kp16 = static_cast<const unsigned short*>(a.k) + kv_base * D;
   const unsigned short* vp16 = static_cast<const unsigned short*>(a.v) + kv_base * D;
-  const int8_t* kp8 = static_cast<const int8_t*>(a.k) + kv_base * D;
-  const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
   const int last_key = a.s_k - 1;
 
-  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks (8 bytes for int8 codes),
-  // double-buffered in registers, and written to LDS at row r, physical chunk lc ^ swz(r).
-  // int8 codes are converted exactly (K -> bf16, V -> fp16) on the way.
+  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks, double-buffered in
+  // registers, and written to LDS at row r, physical chunk lc ^ swz(r).  The loads are issued
+  // unconditionally (rows past the last key repeat it; those keys are masked in the softmax) so
+  // that the code stays straight-line and the first MFMA of a tile does not wait for them.
   u32x4 kreg[CH], vreg[CH];
-  float sreg = 0.f;
   auto load_tile = [&](int t) {
     const int k0 = (t_lo + t) * BN;
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int idx = tid + 64 * NW * u;
+      const int idx = min(tid + 64 * NW * u, BN * NC - 1);
       const int r = idx / NC, lc = idx % NC;
-      u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-      if ((BN * NC % (64 * NW) == 0 || idx < BN * NC) && k0 + r < a.s_k) {
-        if constexpr (KV_I8) {
-          const u32x2 k2 = *reinterpret_cast<const u32x2*>(kp8 + (int64_t)(k0 + r) * D + 8 * lc);
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(vp8 + (int64_t)(k0 + r) * D + 8 * lc);
-          wk[0] = k2[0];
-          wk[1] = k2[1];
-          wv[0] = v2[0];
-          wv[1] = v2[1];
-        } else {
-          wk = *reinterpret_cast<const u32x4*>(kp16 + (int64_t)(k0 + r) * D + 8 * lc);
-          wv = *reinterpret_cast<const u32x4*>(vp16 + (int64_t)(k0 + r) * D + 8 * lc);
-        }
-      }
-      kreg[u] = wk;
-      vreg[u] = wv;
-    }
-    if (KV_I8 && tid < 2 * BN) {
-      const int j = k0 + (tid % BN);
-      sreg = 0.f;
-      if (j < a.s_k) sreg = tid < BN ? a.k_scale[kv_base + j] : a.v_scale[kv_base + j] * vs_norm;
+      const int64_t row = min(k0 + r, last_key);
+      kreg[u] = *reinterpret_cast<const u32x4*>(kp16 + row * D + 8 * lc);
+      vreg[u] = *reinterpret_cast<const u32x4*>(vp16 + row * D + 8 * lc);
     }
   };
   auto store_tile = [&](int st) {
@@ -198,20 +150,9 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
         const int r = idx / NC, lc = idx % NC;
         const int pc = lc ^ swz<SWZ>(r);
-        u32x4 kw = kreg[u], vw = vreg[u];
-        if constexpr (KV_I8) {
-          const u32x2 k0v = i8x4_to_bf16x4(kreg[u][0]), k1v = i8x4_to_bf16x4(kreg[u][1]);
-          const u32x2 v0v = i8x4_to_f16x4(vreg[u][0]), v1v = i8x4_to_f16x4(vreg[u][1]);
-          kw = u32x4{k0v[0], k0v[1], k1v[0], k1v[1]};
-          vw = u32x4{v0v[0], v0v[1], v1v[0], v1v[1]};
-        }
-        *reinterpret_cast<u32x4*>(lds_k[st] + r * D + 8 * pc) = kw;
-        *reinterpret_cast<u32x4*>(lds_v[st] + r * D + 8 * pc) = vw;
+        *reinterpret_cast<u32x4*>(lds_k[st] + r * D + 8 * pc) = kreg[u];
+        *reinterpret_cast<u32x4*>(lds_v[st] + r * D + 8 * pc) = vreg[u];
       }
-    }
-    if (KV_I8 && tid < 2 * BN) {
-      if (tid < BN) lds_ks[st][tid] = sreg;
-      else lds_vs[st][tid - BN] = sreg;
     }
   };
 
@@ -234,9 +175,11 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   }
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  // one tile; for head_dim <= 128 the LDS stage is a compile-time constant, so every LDS address
+  // is a per-lane base plus an immediate offset
+  auto step = [&](const int t, auto stage) {
+    const int st = static_cast<int>(stage);
+    load_tile(min(t + 1, n_tiles - 1));
 
     const int k0 = (t_lo + t) * BN;
     bool skip = !wave_live;
@@ -282,14 +225,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
           }
         }
 
-        if constexpr (KV_I8) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[st][32 * kb + 8 * g4 + 4 * h]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[4 * g4 + e] *= sc[e];
-          }
-        }
         if (need_mask) {
           // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
           const int kl0 = k0 + 32 * kb + 4 * h;
@@ -330,41 +265,37 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
         l_run += ps;
         // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7]
         u32x4 Pw[2];
-        if constexpr (KV_I8) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[st][32 * kb + 8 * g4 + 4 * h]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[4 * g4 + e] *= sc[e];
-          }
-#pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_f16x2(p[2 * q2], p[2 * q2 + 1]);
-        } else {
-#pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
-        }
+        for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
 
         // O^T[db] += V^T P^T
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            if constexpr (KV_I8)
-              O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf[s2][db]), __builtin_bit_cast(f16x8, Pw[s2]), O[db]);
-            else
-              O[db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf[s2][db]), __builtin_bit_cast(bf16x8, Pw[s2]), O[db]);
+            O[db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf[s2][db]), __builtin_bit_cast(bf16x8, Pw[s2]), O[db]);
           }
       }
     }
 
     if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
     __syncthreads();
+  };
+  if constexpr (D <= 128) {
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, std::integral_constant<int, 0>{});
+      step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
+  } else {
+    // wider heads already use the whole register file; the stage stays a loop variable
+    for (int t = 0; t < n_tiles; ++t) step(t, t & 1);
   }
 
   // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
   const float l_tot = l_run + xor32(l_run);
   float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
-  if constexpr (KV_I8) inv *= vs_unnorm;
   if (qi < a.s_q) {
     float y[NDB * 16];
 #pragma unroll
@@ -391,34 +322,29 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   }
 }
 
+
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, int32_t kv_dtype, hipStream_t st, const char** name) {
+hipError_t launch_d(const PrefillArgs& a, hipStream_t st, const char** name) {
   const int64_t n_qb = (a.s_q + Cfg<D>::BM - 1) / Cfg<D>::BM;
   const int64_t blocks = n_qb * a.bh_q;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (kv_dtype == kI8) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
-    *name = "prefill_bf16_i8kv";
-  } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
-    *name = "prefill_bf16";
-  }
+  hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
+  *name = "prefill_bf16";
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, int32_t kv_dtype, hipStream_t stream,
-                               const char** name) {
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name) {
   switch (d) {
-    case 32: return launch_d<32>(a, kv_dtype, stream, name);
-    case 64: return launch_d<64>(a, kv_dtype, stream, name);
-    case 96: return launch_d<96>(a, kv_dtype, stream, name);
-    case 128: return launch_d<128>(a, kv_dtype, stream, name);
-    case 160: return launch_d<160>(a, kv_dtype, stream, name);
-    case 192: return launch_d<192>(a, kv_dtype, stream, name);
-    case 224: return launch_d<224>(a, kv_dtype, stream, name);
-    case 256: return launch_d<256>(a, kv_dtype, stream, name);
+    case 32: return launch_d<32>(a, stream, name);
+    case 64: return launch_d<64>(a, stream, name);
+    case 96: return launch_d<96>(a, stream, name);
+    case 128: return launch_d<128>(a, stream, name);
+    case 160: return launch_d<160>(a, stream, name);
+    case 192: return launch_d<192>(a, stream, name);
+    case 224: return launch_d<224>(a, stream, name);
+    case 256: return launch_d<256>(a, stream, name);
     default: return hipErrorInvalidValue;
   }
 }

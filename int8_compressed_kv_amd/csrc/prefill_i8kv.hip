@@ -1,0 +1,399 @@
+// Attention forward on gfx950 MFMA over the per-token int8 KV cache, for bf16 Q (the plain
+// bf16 variant is prefill_bf16.hip, which shares this layout and schedule).
+//
+// Method: FlashAttention-2 style tiled forward with an online softmax (fkl.flash_attention
+// PR, Summary: FA-2 forward, fp32 accumulation, compressed int8 KV dequantized inside q.k and
+// p.v; Foundry attention/ README, References: the online-softmax recurrence).  For each key
+// tile, with running row max m, running sum l and accumulator O:
+//   S = sigma * k_s Q K~^T (masked) ; m' = max(m, rowmax S) ; P = exp(S - m') ;
+//   l = exp(m - m') l + rowsum P ; O = exp(m - m') O + (P v_s) V~.
+// Finally O / l, the epilogue ops in fp32, and the store.
+//
+// gfx950 mapping
+//   * A workgroup is 8 waves = 256 query rows (4 waves for head_dim > 128, whose fragments
+//     need the whole register file); each wave owns 32 rows and keeps their Q fragments in
+//     registers.  Two waves per SIMD: while one runs the softmax on the vector ALU the other
+//     keeps the matrix core busy.
+//   * The int8 codes are converted exactly to bf16 (K) and fp16 (V) on their way from the
+//     staging registers into LDS -- the compressed cache is never expanded in global memory.
+//     K and V tiles of 64 keys live in LDS row-major, 16-byte chunks XOR-swizzled by row so
+//     that both operand reads below are free of bank conflicts.  Tiles are double-buffered:
+//     the global loads of tile t+1 are in flight (in registers) while tile t is computed, then
+//     converted and written to the other LDS stage; one barrier per tile.
+//   * S^T = K Q^T (keys = MFMA rows, queries = columns) on v_mfma_f32_32x32x16_bf16: each
+//     query's scores sit in one lane pair, so the row max needs one exchange; k_s scales S in
+//     registers.  P~^T = fp16(P v_s 2^-E) in the accumulator layout is the B operand of
+//     O^T += V~^T P~^T on v_mfma_f32_32x32x16_f16; E is a power of two from the largest v_s
+//     the block visits (keeps P v_s in fp16 range) and O is multiplied back by 2^E at the end.
+//     The V~^T operand (8 keys of one head-dim column per lane) comes from two transposing
+//     LDS reads (ds_read_b64_tr_b16) of the row-major tile.
+//   * The running max is only raised when a row's tile max exceeds it by more than 2^8 in the
+//     exp2 domain; otherwise the stale max is kept (O and l stay mutually consistent, the O
+//     rescale is skipped) and P stays below 2^8.
+//   * Tiles wholly outside a wave's causal / window band are skipped; element masks are
+//     applied only on boundary tiles.  Blocks run longest-first under causal masks and are
+//     dealt to the 8 XCDs so that the G query heads sharing a KV head stay on one XCD.
+#include "device_common.hpp"
+
+namespace fa {
+namespace {
+
+typedef short s16x4v __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
+
+template <int D>
+struct Cfg {
+  static constexpr int NW = D <= 128 ? 8 : 4;    // waves per workgroup (2 or 1 per SIMD)
+  static constexpr int BM = 32 * NW;             // query rows per workgroup
+  static constexpr int BN = 64;                  // keys per LDS tile
+  static constexpr int NC = D / 8;               // 16-byte chunks per row
+  static constexpr int TILE = BN * D;            // 16-bit elements per K or V tile
+  static constexpr int SWZ = (NC % 16 == 0) ? 16 : (NC % 8 == 0) ? 8 : 4;   // swizzle span
+  static constexpr int CH = (BN * NC + 64 * NW - 1) / (64 * NW);   // chunks per thread per matrix
+  static constexpr float kLazyLog2 = 8.0f;       // stale-max headroom, exp2 domain
+};
+
+// chunk permutation of row r: rows r..r+3 land in disjoint 4-chunk groups, 16 rows in 16
+// distinct chunks.
+template <int SWZ>
+__device__ __forceinline__ int swz(int r) {
+  return (((r & 3) << 2) | ((r >> 2) & 3)) & (SWZ - 1);
+}
+
+__device__ __forceinline__ unsigned gather_byte(unsigned w0, unsigned w1, unsigned w2, unsigned w3, int b) {
+  const unsigned s = 8u * b;
+  return ((w0 >> s) & 0xffu) | (((w1 >> s) & 0xffu) << 8) | (((w2 >> s) & 0xffu) << 16) |
+         (((w3 >> s) & 0xffu) << 24);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(PrefillArgs a) {
+  using C = Cfg<D>;
+  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, NST = 2, CH = C::CH;
+  constexpr int SWZ = C::SWZ;
+  constexpr int NKS = D / 16;   // 16-deep k-steps of Q.K
+  constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O
+
+  __shared__ __attribute__((aligned(16))) unsigned short lds_k[NST][C::TILE];
+  __shared__ __attribute__((aligned(16))) unsigned short lds_v[NST][C::TILE];
+  __shared__ __attribute__((aligned(16))) float lds_ks[NST][BN];
+  __shared__ __attribute__((aligned(16))) float lds_vs[NST][BN];
+  __shared__ float lds_red[NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;       // half of the wave (MFMA k-slot group)
+  const int c = lane & 31;       // MFMA column (query) / row (key, head-dim)
+  const int g16 = lane >> 4;     // 16-lane group of the transposing reads
+  const int i16 = lane & 15;
+
+  // ---- block -> (query block, head): longest-first, KV groups kept on one XCD
+  const int G = a.group;
+  const int n_qb = (a.s_q + BM - 1) / BM;
+  const int64_t chunks = (int64_t)n_qb * a.bh_kv;
+  const int64_t full = (chunks / 8) * 8 * G;
+  const int64_t b = blockIdx.x;
+  int64_t chunk;
+  int g;
+  if (b < full) {
+    const int64_t x = b % 8, j = b / 8;
+    chunk = 8 * (j / G) + x;
+    g = (int)(j % G);
+  } else {
+    chunk = b / G;
+    g = (int)(b % G);
+  }
+  const int rank = (int)(chunk / a.bh_kv);
+  const int kvh = (int)(chunk % a.bh_kv);
+  const int qblk = a.causal ? n_qb - 1 - rank : rank;
+  const int head = kvh * G + g;
+  const int q0 = qblk * BM;
+  const int off = a.s_k - a.s_q;
+
+  // ---- key range of the block
+  const int r_last = min(q0 + BM, a.s_q) - 1;
+  int lo = 0, hi = a.s_k;
+  if (a.causal) hi = max(0, min(a.s_k, r_last + off + 1));
+  if (a.window) lo = max(0, q0 + off - a.window + 1);
+  const int t_lo = lo / BN;
+  const int n_tiles = hi > lo ? (hi + BN - 1) / BN - t_lo : 0;
+  const int64_t kv_base = (int64_t)kvh * a.s_k;
+
+  // ---- int8: power-of-two normalisation for P * v_s (largest v_s over [lo, hi))
+  float vs_norm = 1.f, vs_unnorm = 1.f;
+  float mx = 0.f;
+  for (int j = lo + tid; j < hi; j += 64 * NW) mx = fmaxf(mx, a.v_scale[kv_base + j]);
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
+  if (lane == 0) lds_red[wave] = mx;
+  __syncthreads();
+  mx = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_red[w]);
+  int e = 0;
+  if (mx > 0.f) (void)frexpf(mx, &e);   // mx = f * 2^e, f in [0.5, 1)
+  vs_norm = ldexpf(1.f, -e);
+  vs_unnorm = ldexpf(1.f, e);
+
+
+  // ---- Q fragments (B operand of S^T): Qf[ks] = Q[qw0 + c][16 ks + 8 h .. + 8]
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + c;
+  const unsigned short* qp = static_cast<const unsigned short*>(a.q) + (int64_t)head * a.s_q * D;
+  bf16x8 Qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qi < a.s_q) w = *reinterpret_cast<const u32x4*>(qp + (int64_t)qi * D + 16 * ks + 8 * h);
+    Qf[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+
+  const int8_t* kp8 = static_cast<const int8_t*>(a.k) + kv_base * D;
+  const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
+  const int last_key = a.s_k - 1;
+
+  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks (8 bytes for int8 codes),
+  // double-buffered in registers, and written to LDS at row r, physical chunk lc ^ swz(r).
+  // int8 codes are converted exactly (K -> bf16, V -> fp16) on the way.
+  u32x4 kreg[CH], vreg[CH];
+  float sreg = 0.f;
+  auto load_tile = [&](int t) {
+    const int k0 = (t_lo + t) * BN;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = tid + 64 * NW * u;
+      const int r = idx / NC, lc = idx % NC;
+      u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
+      if ((BN * NC % (64 * NW) == 0 || idx < BN * NC) && k0 + r < a.s_k) {
+        const u32x2 k2 = *reinterpret_cast<const u32x2*>(kp8 + (int64_t)(k0 + r) * D + 8 * lc);
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(vp8 + (int64_t)(k0 + r) * D + 8 * lc);
+        wk[0] = k2[0];
+        wk[1] = k2[1];
+        wv[0] = v2[0];
+        wv[1] = v2[1];
+      }
+      kreg[u] = wk;
+      vreg[u] = wv;
+    }
+    if (tid < 2 * BN) {
+      const int j = k0 + (tid % BN);
+      sreg = 0.f;
+      if (j < a.s_k) sreg = tid < BN ? a.k_scale[kv_base + j] : a.v_scale[kv_base + j] * vs_norm;
+    }
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = tid + 64 * NW * u;
+      if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
+        const int r = idx / NC, lc = idx % NC;
+        const int pc = lc ^ swz<SWZ>(r);
+        const u32x2 k0v = i8x4_to_bf16x4(kreg[u][0]), k1v = i8x4_to_bf16x4(kreg[u][1]);
+        const u32x2 v0v = i8x4_to_f16x4(vreg[u][0]), v1v = i8x4_to_f16x4(vreg[u][1]);
+        const u32x4 kw = {k0v[0], k0v[1], k1v[0], k1v[1]};
+        const u32x4 vw = {v0v[0], v0v[1], v1v[0], v1v[1]};
+        *reinterpret_cast<u32x4*>(lds_k[st] + r * D + 8 * pc) = kw;
+        *reinterpret_cast<u32x4*>(lds_v[st] + r * D + 8 * pc) = vw;
+      }
+    }
+    if (tid < 2 * BN) {
+      if (tid < BN) lds_ks[st][tid] = sreg;
+      else lds_vs[st][tid - BN] = sreg;
+    }
+  };
+
+  // ---- per-wave state
+  f32x16 O[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+  float m_run = neg_inf(), l_run = 0.f, mc = 0.f;
+  const float c2 = a.scale_log2;
+  const float lazy_thr = C::kLazyLog2 / c2;   // raw-score headroom before the max is raised
+  const int w_last = qw0 + 31;
+  const bool wave_live = qw0 < a.s_q;
+
+  // ---- pipeline: the global loads of tile t+1 are in flight while tile t is computed
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    const int k0 = (t_lo + t) * BN;
+    bool skip = !wave_live;
+    if (a.causal && k0 > w_last + off) skip = true;
+    if (a.window && k0 + BN - 1 <= qw0 + off - a.window) skip = true;
+    if (!skip) {
+      const bool need_mask = (k0 + BN > a.s_k) || (a.causal && k0 + BN - 1 > qw0 + off) ||
+                             (a.window && k0 <= w_last + off - a.window);
+      const unsigned short* Kt = lds_k[st];
+      const unsigned short* Vt = lds_v[st];
+
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T: lane holds keys 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative) for query qi
+        bf16x8 kf[NKS];
+        const int krow = 32 * kb + c;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          kf[ks] = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
+        f32x16 S;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) S = mfma32_bf16(kf[ks], Qf[ks], S);
+
+        // V^T fragments for this 32-key step: vf[s2][db] holds keys kbase + 0..3 and
+        // kbase + 8 + 0..3 (kbase = 32 kb + 16 s2 + 4 h) of head-dim 32 db + c
+        u32x4 vf[2][NDB];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+            const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
+            const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
+            const s16x4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0));
+            const s16x4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+            vf[s2][db] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+          }
+        }
+
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[st][32 * kb + 8 * g4 + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[4 * g4 + e] *= sc[e];
+        }
+
+        if (need_mask) {
+          // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
+          const int kl0 = k0 + 32 * kb + 4 * h;
+          int hi_i = a.s_k - 1 - kl0;
+          if (a.causal) hi_i = min(hi_i, qi + off - kl0);
+          int lo_i = a.window ? qi + off - a.window + 1 - kl0 : -0x40000000;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ko = 8 * (i / 4) + (i % 4);
+            if (ko > hi_i || ko < lo_i) S[i] = neg_inf();
+          }
+        }
+
+        // online softmax with a lazily raised max
+        float mx = neg_inf();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+        mx = fmaxf(mx, xor32(mx));
+        if (__any(mx - m_run > lazy_thr)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+          m_run = m_new;
+          mc = m_use * c2;
+        }
+        float p[16];
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -mc));
+          ps += p[i];
+        }
+        l_run += ps;
+        // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7]
+        u32x4 Pw[2];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[st][32 * kb + 8 * g4 + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[4 * g4 + e] *= sc[e];
+        }
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_f16x2(p[2 * q2], p[2 * q2 + 1]);
+
+        // O^T[db] += V^T P^T
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf[s2][db]), __builtin_bit_cast(f16x8, Pw[s2]), O[db]);
+          }
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
+    __syncthreads();
+  }
+
+  // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
+  const float l_tot = l_run + xor32(l_run);
+  float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
+  inv *= vs_unnorm;
+  if (qi < a.s_q) {
+    float y[NDB * 16];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[16 * db + i] = O[db][i] * inv;
+    apply_epilogue_all(y, a.epi);
+    const int64_t row = (int64_t)head * a.s_q + qi;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        const float* yy = y + 16 * db + 4 * g4;
+        if (a.out_bf16) {
+          const u32x2 w = {pack_bf16x2(yy[0], yy[1]), pack_bf16x2(yy[2], yy[3])};
+          *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + d0) = w;
+        } else {
+          const f32x4 w = {yy[0], yy[1], yy[2], yy[3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = w;
+        }
+      }
+    if (a.lse && h == 0) a.lse[row] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : neg_inf();
+  }
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t st, const char** name) {
+  const int64_t n_qb = (a.s_q + Cfg<D>::BM - 1) / Cfg<D>::BM;
+  const int64_t blocks = n_qb * a.bh_q;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_i8kv_kernel<D>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
+  *name = "prefill_bf16_i8kv";
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_i8kv(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name) {
+  switch (d) {
+    case 32: return launch_d<32>(a, stream, name);
+    case 64: return launch_d<64>(a, stream, name);
+    case 96: return launch_d<96>(a, stream, name);
+    case 128: return launch_d<128>(a, stream, name);
+    case 160: return launch_d<160>(a, stream, name);
+    case 192: return launch_d<192>(a, stream, name);
+    case 224: return launch_d<224>(a, stream, name);
+    case 256: return launch_d<256>(a, stream, name);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa
