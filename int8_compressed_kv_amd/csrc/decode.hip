@@ -144,8 +144,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(qv[kk][i]));
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     int E = 0;
     if (mx > 0.f) {
       (void)frexpf(mx, &E);   // mx = f * 2^E, f in [0.5, 1)
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     if (__any(mx - m_run > lazy_thr)) {
       flush();
       const float m_new = fmaxf(m_run, mx);
@@ -338,8 +338,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         pmax = fmaxf(pmax, pt[kb][v]);
       }
     l_run += ps;
-    pmax = fmaxf(pmax, xor16(pmax));
-    pmax = fmaxf(pmax, xor32(pmax));
+    pmax = max_xor16(pmax);
+    pmax = max_xor32(pmax);
     int Fp = -1000;
     if (pmax > 0.f) (void)frexpf(pmax, &Fp);    // pmax < 2^Fp
     if (__any(Fp > F) || since_flush >= kFlushTiles) {
@@ -407,8 +407,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
 #pragma unroll
     for (int v = 0; v < 4; ++v) O[b][v] = Of[b][v];
   float lt = l_run;
-  lt = lt + xor16(lt);
-  lt = lt + xor32(lt);
+  lt = add_xor16(lt);
+  lt = add_xor32(lt);
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll

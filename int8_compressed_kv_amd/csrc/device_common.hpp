@@ -90,12 +90,25 @@ __device__ __forceinline__ u32x2 i8x4_to_f16x4(unsigned w) {
 // ---------------------------------------------------------------------------------------
 // Cross-lane exchanges
 // ---------------------------------------------------------------------------------------
-// value held by lane l ^ 32
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Reductions across lane pairs (l, l ^ 32) and (l, l ^ 16), on the VALU: v_permlane32_swap /
+// v_permlane16_swap with both operands x leave x's partner value in one of the two results and
+// x itself in the other, so a symmetric op of the two results is the pair reduction on every
+// lane (no LDS round trip as with ds_bpermute).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xor16(float x) {
-  return __shfl_xor(x, 16, 64);
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------------------

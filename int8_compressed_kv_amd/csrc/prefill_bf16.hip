@@ -40,6 +40,9 @@ namespace {
 typedef short s16x4v __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 
+// dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format; no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+
 template <int D>
 struct Cfg {
   static constexpr int NW = D <= 128 ? 8 : 4;    // waves per workgroup (2 or 1 per SIMD)
@@ -125,22 +128,31 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
 
   const unsigned short* kp16 = static_cast<const unsigned short*>(a.k) + kv_base * D;
   const unsigned short* vp16 = static_cast<const unsigned short*>(a.v) + kv_base * D;
-  const int last_key = a.s_k - 1;
 
-  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks, double-buffered in
-  // registers, and written to LDS at row r, physical chunk lc ^ swz(r).  The loads are issued
-  // unconditionally (rows past the last key repeat it; those keys are masked in the softmax) so
-  // that the code stays straight-line and the first MFMA of a tile does not wait for them.
+  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks with buffer loads (a
+  // scalar resource per tile, based at row k0 and ending at the head's last key, plus a constant
+  // per-lane offset: no vector address arithmetic, and rows past the end read as zero -- those
+  // keys are masked in the softmax), double-buffered in registers, and written to LDS at row r,
+  // physical chunk lc ^ swz(r).
   u32x4 kreg[CH], vreg[CH];
+  int soff[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int idx = min(tid + 64 * NW * u, BN * NC - 1);
+    soff[u] = ((idx / NC) * D + 8 * (idx % NC)) * 2;
+  }
   auto load_tile = [&](int t) {
     const int k0 = (t_lo + t) * BN;
+    const int64_t rem = (int64_t)(a.s_k - k0) * D * 2;
+    const int nrec = (int)(rem < 0x7fffffff ? rem : 0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(kp16 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(vp16 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int idx = min(tid + 64 * NW * u, BN * NC - 1);
-      const int r = idx / NC, lc = idx % NC;
-      const int64_t row = min(k0 + r, last_key);
-      kreg[u] = *reinterpret_cast<const u32x4*>(kp16 + row * D + 8 * lc);
-      vreg[u] = *reinterpret_cast<const u32x4*>(vp16 + row * D + 8 * lc);
+      kreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, soff[u], 0, 0));
+      vreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, soff[u], 0, 0));
     }
   };
   auto store_tile = [&](int st) {
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
         float mx = neg_inf();
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-        mx = fmaxf(mx, xor32(mx));
+        mx = max_xor32(mx);
         if (__any(mx - m_run > lazy_thr)) {
           const float m_new = fmaxf(m_run, mx);
           const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
@@ -256,17 +268,18 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
           mc = m_use * c2;
         }
         float p[16];
-        float ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -mc));
-          ps += p[i];
-        }
-        l_run += ps;
-        // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7]
+        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -mc));
+        // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7].  The row sum is taken over the
+        // bf16-rounded P the MFMA multiplies, two values per v_dot2 with ones.
         u32x4 Pw[2];
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
+        for (int q2 = 0; q2 < 8; ++q2) {
+          const unsigned w = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
+          Pw[q2 / 4][q2 % 4] = w;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
+        }
 
         // O^T[db] += V^T P^T
 #pragma unroll
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   }
 
   // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = add_xor32(l_run);
   float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
   if (qi < a.s_q) {
     float y[NDB * 16];

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       S[i] = s;
       tmax = fmaxf(tmax, s);
     }
-    tmax = fmaxf(tmax, xor32(tmax));
+    tmax = max_xor32(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   }
 
   // finalize: O / l, epilogue, store; LSE = m * sigma + ln(l)
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = add_xor32(l_run);
   const float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
   if (qi < a.s_q) {
     const int64_t row = (int64_t)head * a.s_q + qi;

@@ -41,6 +41,9 @@ namespace {
 typedef short s16x4v __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 
+// dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format; no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+
 template <int D>
 struct Cfg {
   static constexpr int NW = D <= 128 ? 8 : 4;    // waves per workgroup (2 or 1 per SIMD)
@@ -153,34 +156,37 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
   const int last_key = a.s_k - 1;
 
-  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks (8 bytes for int8 codes),
-  // double-buffered in registers, and written to LDS at row r, physical chunk lc ^ swz(r).
-  // int8 codes are converted exactly (K -> bf16, V -> fp16) on the way.
-  u32x4 kreg[CH], vreg[CH];
+  // ---- staging: tile rows k0 .. k0 + 63 are read as 8-byte chunks of codes with buffer loads
+  // (a scalar resource per tile, based at row k0 and ending at the head's last key, plus a
+  // constant per-lane offset; rows past the end read as zero and are masked in the softmax),
+  // double-buffered in registers, converted exactly (K -> bf16, V -> fp16) and written to LDS at
+  // row r, physical chunk lc ^ swz(r).  Waves 0 and 1 also fetch the tile's k and v scales.
+  u32x2 kreg[CH], vreg[CH];
+  int soff[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int idx = min(tid + 64 * NW * u, BN * NC - 1);
+    soff[u] = (idx / NC) * D + 8 * (idx % NC);
+  }
+  const float* scale_src = (wave & 1) ? a.v_scale : a.k_scale;
+  const float scale_mul = (wave & 1) ? vs_norm : 1.f;
   float sreg = 0.f;
   auto load_tile = [&](int t) {
     const int k0 = (t_lo + t) * BN;
+    const int64_t rem = (int64_t)(a.s_k - k0) * D;
+    const int nrec = (int)(rem < 0x7fffffff ? rem : 0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kp8 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(vp8 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int idx = tid + 64 * NW * u;
-      const int r = idx / NC, lc = idx % NC;
-      u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-      if ((BN * NC % (64 * NW) == 0 || idx < BN * NC) && k0 + r < a.s_k) {
-        const u32x2 k2 = *reinterpret_cast<const u32x2*>(kp8 + (int64_t)(k0 + r) * D + 8 * lc);
-        const u32x2 v2 = *reinterpret_cast<const u32x2*>(vp8 + (int64_t)(k0 + r) * D + 8 * lc);
-        wk[0] = k2[0];
-        wk[1] = k2[1];
-        wv[0] = v2[0];
-        wv[1] = v2[1];
-      }
-      kreg[u] = wk;
-      vreg[u] = wv;
+      kreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, soff[u], 0, 0));
+      vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, soff[u], 0, 0));
     }
-    if (tid < 2 * BN) {
-      const int j = k0 + (tid % BN);
-      sreg = 0.f;
-      if (j < a.s_k) sreg = tid < BN ? a.k_scale[kv_base + j] : a.v_scale[kv_base + j] * vs_norm;
-    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(scale_src + kv_base + k0), 0, (a.s_k - k0) * 4, kBufferFlags);
+    sreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0)) * scale_mul;
   };
   auto store_tile = [&](int st) {
 #pragma unroll
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
         float mx = neg_inf();
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-        mx = fmaxf(mx, xor32(mx));
+        mx = max_xor32(mx);
         if (__any(mx - m_run > lazy_thr)) {
           const float m_new = fmaxf(m_run, mx);
           const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   }
 
   // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = add_xor32(l_run);
   float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
   inv *= vs_unnorm;
   if (qi < a.s_q) {
