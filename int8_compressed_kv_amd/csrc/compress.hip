@@ -3,7 +3,8 @@
 //
 // Per token: a = max|x| (exact), s = a / 127 with one IEEE fp32 division, code =
 // rint(x / s) with the IEEE fp32 quotient (ties to even), clamped to [-127, 127];
-// an all-zero token gets s = 0 and codes 0.
+// an all-zero token gets s = 0 and codes 0.  The quotients are computed exactly as IEEE
+// division would round them, from a correctly rounded reciprocal and one fma correction.
 //
 // HBM-bound streaming kernel: a token row is owned by a segment of lanes, each lane
 // reading 16 contiguous bytes, so a wave's load covers whole rows with full coalescing.
@@ -14,6 +15,29 @@ namespace fa {
 namespace {
 
 constexpr int pow2_at_least(int r) { return r <= 1 ? 1 : 2 * pow2_at_least((r + 1) / 2); }
+
+template <int N>
+__device__ __forceinline__ float dpp_row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// max over aligned groups of SEG lanes.  Groups of 16 or more use DPP rotations within each
+// 16-lane row and the row / half-wave swaps (all VALU); smaller groups use lane shuffles.
+template <int SEG>
+__device__ __forceinline__ float segment_max(float a) {
+  if constexpr (SEG >= 16) {
+    a = fmaxf(a, dpp_row_ror<8>(a));
+    a = fmaxf(a, dpp_row_ror<4>(a));
+    a = fmaxf(a, dpp_row_ror<2>(a));
+    a = fmaxf(a, dpp_row_ror<1>(a));
+    if constexpr (SEG >= 32) a = max_xor16(a);
+    if constexpr (SEG >= 64) a = max_xor32(a);
+  } else {
+#pragma unroll
+    for (int off = SEG / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  }
+  return a;
+}
 
 template <int D, bool BF16_IN, int U>
 __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ xin, int64_t n,
@@ -32,27 +56,26 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
   const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * 256) >> 6;
 
+  // loads are issued unconditionally (rows past the end repeat the last row, idle lanes of a
+  // segment repeat its last chunk) so the code stays straight-line; only the stores are guarded.
+  // Loads and stores are nontemporal: every byte is touched once.
+  const int chunk = lane_on ? seg_lane : R - 1;
   for (int64_t base = wave * (RPW * U); base < n; base += nwaves * (RPW * U)) {
     float x[U][ELEM];
-    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = base + (int64_t)u * RPW + sub;
-      ok[u] = lane_on && row < n;
+      const int64_t row = min(base + (int64_t)u * RPW + sub, n - 1);
       if (BF16_IN) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (ok[u])
-          w = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(xin) + row * D +
-                                              seg_lane * ELEM);
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            static_cast<const unsigned short*>(xin) + row * D + chunk * ELEM));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[u][2 * e] = __uint_as_float(w[e] << 16);
           x[u][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
         }
       } else {
-        f32x4 w = {0.f, 0.f, 0.f, 0.f};
-        if (ok[u])
-          w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xin) + row * D + seg_lane * ELEM);
+        const f32x4 w = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(static_cast<const float*>(xin) + row * D + chunk * ELEM));
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[u][e] = w[e];
       }
@@ -62,33 +85,46 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < ELEM; ++e) a = fmaxf(a, fabsf(x[u][e]));
-#pragma unroll
-      for (int off = SEG / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      a = segment_max<SEG>(a);
       const float s = __fdiv_rn(a, 127.0f);
+      // code = rint(RN(x / s)) clamped to [-127, 127].  The correctly rounded quotient comes from
+      // the correctly rounded reciprocal y = RN(1 / s) and one correction step (Markstein):
+      // q0 = RN(x y) is within an ulp of x / s, the residual e = x - s q0 is exact in one fma,
+      // and RN(q0 + e y) = RN(x / s).  It needs no over- or underflow, which holds for
+      // s >= 2^-64 (|x / s| <= 127 + 2^-16 here); smaller nonzero scales take the IEEE division.
+      const float y = __fdiv_rn(1.0f, s);
+      float c[ELEM];
+#pragma unroll
+      for (int e = 0; e < ELEM; ++e) {
+        const float q0 = x[u][e] * y;
+        const float r = __builtin_fmaf(-s, q0, x[u][e]);
+        c[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(__builtin_fmaf(r, y, q0)), -127.f, 127.f);
+      }
+      if (__builtin_expect(__any(s < 0x1p-64f && s > 0.f), 0)) {
+#pragma unroll
+        for (int e = 0; e < ELEM; ++e)
+          if (s < 0x1p-64f) c[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(__fdiv_rn(x[u][e], s)), -127.f, 127.f);
+      }
       unsigned packed[ELEM / 4];
 #pragma unroll
       for (int e4 = 0; e4 < ELEM / 4; ++e4) {
         unsigned w = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          float c = 0.f;
-          if (s > 0.f) {
-            c = __builtin_rintf(__fdiv_rn(x[u][4 * e4 + b], s));
-            c = fminf(fmaxf(c, -127.f), 127.f);
-          }
-          w |= ((unsigned)((int)c) & 0xffu) << (8 * b);
+          const int ci = s > 0.f ? (int)c[4 * e4 + b] : 0;   // an all-zero token: s = 0, codes 0
+          w |= ((unsigned)ci & 0xffu) << (8 * b);
         }
         packed[e4] = w;
       }
       const int64_t row = base + (int64_t)u * RPW + sub;
-      if (ok[u]) {
+      if (lane_on && row < n) {
         if (ELEM == 8) {
-          u32x2 p2 = {packed[0], packed[ELEM / 4 - 1]};
-          *reinterpret_cast<u32x2*>(qout + row * D + seg_lane * ELEM) = p2;
+          const u32x2 p2 = {packed[0], packed[ELEM / 4 - 1]};
+          __builtin_nontemporal_store(p2, reinterpret_cast<u32x2*>(qout + row * D + seg_lane * ELEM));
         } else {
-          *reinterpret_cast<unsigned*>(qout + row * D + seg_lane * ELEM) = packed[0];
+          __builtin_nontemporal_store(packed[0], reinterpret_cast<unsigned*>(qout + row * D + seg_lane * ELEM));
         }
-        if (seg_lane == 0) sout[row] = s;
+        if (seg_lane == 0) __builtin_nontemporal_store(s, sout + row);
       }
     }
   }
@@ -97,12 +133,12 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
 template <int D>
 hipError_t launch_d(const void* x, bool bf16, int64_t n, int8_t* q, float* s, hipStream_t st,
                     const char** name) {
-  constexpr int U = 4;
+  constexpr int U = 4;   // rows per lane segment per loop trip (loads in flight)
   const int elem = bf16 ? 8 : 4;
   const int seg = pow2_at_least(D / elem);
   const int64_t rows_per_block = (int64_t)(256 / 64) * (64 / seg) * U;
   int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
-  const int64_t cap = 256 * 16;   // grid-stride beyond 16 blocks per CU
+  const int64_t cap = 256 * 4;   // grid-stride beyond 4 blocks per CU
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   if (bf16) {
