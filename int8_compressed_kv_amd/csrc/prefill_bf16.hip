@@ -62,10 +62,28 @@ __device__ __forceinline__ int swz(int r) {
   return (((r & 3) << 2) | ((r >> 2) & 3)) & (SWZ - 1);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane l writes the bytes at LDS byte address
+// lds + 16 l.  Written as inline assembly (no output registers: the data goes to LDS) so that
+// the compiler does not add a full wait before every later LDS read; the kernel waits for its
+// own copies (wait_vmcnt0) before the barrier that publishes them.
+__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(0), the other counters unconstrained (gfx9 encoding)
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(PrefillArgs a) {
   using C = Cfg<D>;
-  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, NST = 2, CH = C::CH;
+  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, CH = C::CH;
+  // head_dim 64 and 128: tiles arrive by direct global -> LDS copies into four stages, one
+  // barrier per two tiles; other head dims stage through registers into two stages.
+  constexpr bool DMA = D <= 128 && (BN * NC / 64) % NW == 0;
+  constexpr int NST = DMA ? 4 : 2;
   constexpr int SWZ = C::SWZ;
   constexpr int NKS = D / 16;   // 16-deep k-steps of Q.K
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O
@@ -180,18 +198,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   const int w_last = qw0 + 31;
   const bool wave_live = qw0 < a.s_q;
 
-  // ---- pipeline: the global loads of tile t+1 are in flight while tile t is computed
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  // one tile; for head_dim <= 128 the LDS stage is a compile-time constant, so every LDS address
-  // is a per-lane base plus an immediate offset
-  auto step = [&](const int t, auto stage) {
+  // one tile from LDS stage `stage`; where the stage is a compile-time constant every LDS
+  // address is a per-lane base plus an immediate offset
+  auto compute = [&](const int t, auto stage) {
     const int st = static_cast<int>(stage);
-    load_tile(min(t + 1, n_tiles - 1));
 
     const int k0 = (t_lo + t) * BN;
     bool skip = !wave_live;
@@ -291,19 +301,78 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       }
     }
 
-    if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
-    __syncthreads();
   };
-  if constexpr (D <= 128) {
-    int t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-      step(t, std::integral_constant<int, 0>{});
-      step(t + 1, std::integral_constant<int, 1>{});
+
+  if constexpr (DMA) {
+    // copies of tiles t and t + 1 are issued right after the barrier that ends the compute of
+    // tiles t - 4 and t - 3 (their stages), and are waited for before the barrier ending the
+    // compute of tiles t - 2 and t - 1; between barriers the waves run two tiles unsynchronised
+    constexpr int SPW = (BN * NC / 64) / NW;      // 1-KiB segments per wave per matrix
+    const unsigned short* kp = static_cast<const unsigned short*>(a.k) + kv_base * D;
+    const unsigned short* vp = static_cast<const unsigned short*>(a.v) + kv_base * D;
+    int crow[SPW], ccol[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int p = 64 * (SPW * wave + j) + lane;   // 16-byte position in the tile
+      crow[j] = p / NC;
+      ccol[j] = 8 * ((p % NC) ^ swz<SWZ>(p / NC));  // logical chunk stored at that position
     }
-    if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
+    const unsigned lds_k0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned short*)&lds_k[0][0];
+    const unsigned lds_v0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned short*)&lds_v[0][0];
+    const int last_key = a.s_k - 1;
+    auto copy_tile = [&](int t) {
+      const int k0 = (t_lo + t) * BN;
+      const unsigned st_off = 2u * C::TILE * (unsigned)(t % NST);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
+        const unsigned seg = st_off + 1024u * (unsigned)(SPW * wave + j);
+        copy16_to_lds(kp + row * D + ccol[j], __builtin_amdgcn_readfirstlane(lds_k0 + seg));
+        copy16_to_lds(vp + row * D + ccol[j], __builtin_amdgcn_readfirstlane(lds_v0 + seg));
+      }
+    };
+    auto pair = [&](int t, auto s0, auto s1) {
+      if (t >= n_tiles) return;
+      if (t + 2 < n_tiles) copy_tile(t + 2);
+      if (t + 3 < n_tiles) copy_tile(t + 3);
+      compute(t, s0);
+      if (t + 1 < n_tiles) compute(t + 1, s1);
+      wait_vmcnt0();
+      __syncthreads();
+    };
+    if (n_tiles > 0) copy_tile(0);
+    if (n_tiles > 1) copy_tile(1);
+    wait_vmcnt0();
+    __syncthreads();
+    for (int t = 0; t < n_tiles; t += 4) {
+      pair(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      pair(t + 2, std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
+    }
   } else {
-    // wider heads already use the whole register file; the stage stays a loop variable
-    for (int t = 0; t < n_tiles; ++t) step(t, t & 1);
+    // the global loads of tile t + 1 are in flight (in registers) while tile t is computed
+    auto step = [&](const int t, auto stage) {
+      const int st = static_cast<int>(stage);
+      load_tile(min(t + 1, n_tiles - 1));
+      compute(t, stage);
+      if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
+      __syncthreads();
+    };
+    if (n_tiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
+    __syncthreads();
+    if constexpr (D <= 128) {
+      int t = 0;
+      for (; t + 1 < n_tiles; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+      }
+      if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
+    } else {
+      // wider heads already use the whole register file; the stage stays a loop variable
+      for (int t = 0; t < n_tiles; ++t) step(t, t & 1);
+    }
   }
 
   // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
