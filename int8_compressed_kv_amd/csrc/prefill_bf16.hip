@@ -198,6 +198,28 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   const int w_last = qw0 + 31;
   const bool wave_live = qw0 < a.s_q;
 
+  // V^T fragments of 32-key half kb of a tile: vf[s2][db] holds keys kbase + 0..3 and
+  // kbase + 8 + 0..3 (kbase = 32 kb + 16 s2 + 4 h) of head-dim 32 db + c, from two transposing
+  // LDS reads of the row-major tile
+  auto vread = [&](const unsigned short* Vt, int kb, u32x4 (&vf)[2][NDB]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
+        const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
+        const s16x4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0));
+        const s16x4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+        vf[s2][db] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+      }
+    }
+  };
+
   // one tile from LDS stage `stage`; where the stage is a compile-time constant every LDS
   // address is a per-lane base plus an immediate offset
   auto compute = [&](const int t, auto stage) {
@@ -213,92 +235,89 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       const unsigned short* Kt = lds_k[st];
       const unsigned short* Vt = lds_v[st];
 
+      // S^T of both 32-key halves, two independent MFMA chains: S[kb] lane (c, h) element i holds
+      // key 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative) of query qi
+      f32x16 S[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T: lane holds keys 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative) for query qi
-        bf16x8 kf[NKS];
-        const int krow = 32 * kb + c;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          kf[ks] = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
-        f32x16 S;
+        for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[i] = 0.f;
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) S = mfma32_bf16(kf[ks], Qf[ks], S);
-
-        // V^T fragments for this 32-key step: vf[s2][db] holds keys kbase + 0..3 and
-        // kbase + 8 + 0..3 (kbase = 32 kb + 16 s2 + 4 h) of head-dim 32 db + c
-        u32x4 vf[2][NDB];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-            const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
-            const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
-            const s16x4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0));
-            const s16x4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1));
-            const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
-            vf[s2][db] = u32x4{w0[0], w0[1], w1[0], w1[1]};
-          }
+        for (int kb = 0; kb < 2; ++kb) {
+          const int krow = 32 * kb + c;
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
+          S[kb] = mfma32_bf16(kf, Qf[ks], S[kb]);
         }
 
-        if (need_mask) {
-          // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
+      // V^T fragments of the first 32 keys, read while the softmax runs
+      u32x4 vf0[2][NDB];
+      vread(Vt, 0, vf0);
+
+      if (need_mask) {
+        // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
           const int kl0 = k0 + 32 * kb + 4 * h;
           int hi_i = a.s_k - 1 - kl0;
           if (a.causal) hi_i = min(hi_i, qi + off - kl0);
-          int lo_i = a.window ? qi + off - a.window + 1 - kl0 : -0x40000000;
+          const int lo_i = a.window ? qi + off - a.window + 1 - kl0 : -0x40000000;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int ko = 8 * (i / 4) + (i % 4);
-            if (ko > hi_i || ko < lo_i) S[i] = neg_inf();
+            if (ko > hi_i || ko < lo_i) S[kb][i] = neg_inf();
           }
         }
+      }
 
-        // online softmax with a lazily raised max
-        float mx = neg_inf();
+      // online softmax over the tile's 64 keys with a lazily raised max
+      float mx = neg_inf();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-        mx = max_xor32(mx);
-        if (__any(mx - m_run > lazy_thr)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-          const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-          l_run *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
+      mx = max_xor32(mx);
+      if (__any(mx - m_run > lazy_thr)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+        l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
-          m_run = m_new;
-          mc = m_use * c2;
-        }
-        float p[16];
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -mc));
-        // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7].  The row sum is taken over the
-        // bf16-rounded P the MFMA multiplies, two values per v_dot2 with ones.
-        u32x4 Pw[2];
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+          for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+        m_run = m_new;
+        mc = m_use * c2;
+      }
+      // P^T as B operands: k-step (kb, s2) takes the exponentials of S[kb][8 s2 .. 8 s2 + 7].  The
+      // row sum is taken over the bf16-rounded P the MFMA multiplies, two values per v_dot2.
+      u32x4 Pw[2][2];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int q2 = 0; q2 < 8; ++q2) {
-          const unsigned w = pack_bf16x2(p[2 * q2], p[2 * q2 + 1]);
-          Pw[q2 / 4][q2 % 4] = w;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][2 * q2], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][2 * q2 + 1], c2, -mc));
+          const unsigned w = pack_bf16x2(p0, p1);
+          Pw[kb][q2 / 4][q2 % 4] = w;
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
         }
 
-        // O^T[db] += V^T P^T
+      // O^T[db] += V^T P^T
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            O[db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf[s2][db]), __builtin_bit_cast(bf16x8, Pw[s2]), O[db]);
-          }
-      }
+        for (int db = 0; db < NDB; ++db)
+          O[db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf0[s2][db]), __builtin_bit_cast(bf16x8, Pw[0][s2]), O[db]);
+      u32x4 vf1[2][NDB];
+      vread(Vt, 1, vf1);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          O[db] = mfma32_bf16(__builtin_bit_cast(bf16x8, vf1[s2][db]), __builtin_bit_cast(bf16x8, Pw[1][s2]), O[db]);
     }
 
   };
