@@ -144,3 +144,20 @@ def test_int8_kv_small_and_large_value_scales():
     o = to_np(out)
     check_close(o[0] / 1e-4, ref[0] / 1e-4, TOL_BF16, "small V (relative)")
     check_close(o[1] / 3e4, ref[1] / 3e4, TOL_BF16, "large V (relative)")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_tile_and_pair_boundaries(d):
+    """Key lengths around the 64-key tile and the two-tile copy / barrier grouping (odd and even
+    tile counts, tails of 1 and 63 keys), causal and windowed, with s_q both equal to and below
+    s_k (bottom-right alignment)."""
+    torch = torch_gpu()
+    say(f"bf16 tile/pair boundaries d={d}")
+    cases = [(1, 1), (63, 63), (64, 64), (65, 65), (128, 128), (129, 129), (191, 191), (192, 192),
+             (257, 257), (70, 200), (5, 321)]
+    for i, (s_q, s_k) in enumerate(cases):
+        q, k, v = _inputs(900 + 7 * d + i, 4, 2, s_q, s_k, d)
+        for causal, window in [(True, 0), (False, 0), (True, 65), (True, 130)]:
+            out = _bf16(q, k, v, causal=causal, window=window, out_dtype=torch.float32)
+            ref, _ = oracle.attention(q, k, v, causal=causal, window=window)
+            check_close(to_np(out), ref, TOL_BF16, f"s_q={s_q} s_k={s_k} causal={causal} window={window}")
