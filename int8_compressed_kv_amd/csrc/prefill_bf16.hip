@@ -323,9 +323,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   };
 
   if constexpr (DMA) {
-    // copies of tiles t and t + 1 are issued right after the barrier that ends the compute of
-    // tiles t - 4 and t - 3 (their stages), and are waited for before the barrier ending the
-    // compute of tiles t - 2 and t - 1; between barriers the waves run two tiles unsynchronised
+    // copies of tiles t and t + 1 are issued after a wave's compute of tile t - 2, so after the
+    // barrier that ends the compute of tiles t - 4 and t - 3 (their stages), and are waited for
+    // before the barrier ending the compute of tiles t - 2 and t - 1; between barriers the waves
+    // run two tiles unsynchronised
     constexpr int SPW = (BN * NC / 64) / NW;      // 1-KiB segments per wave per matrix
     const unsigned short* kp = static_cast<const unsigned short*>(a.k) + kv_base * D;
     const unsigned short* vp = static_cast<const unsigned short*>(a.v) + kv_base * D;
@@ -352,9 +353,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
     };
     auto pair = [&](int t, auto s0, auto s1) {
       if (t >= n_tiles) return;
+      compute(t, s0);
+      // issued between the two tiles so that they do not compete with tile t's first LDS reads
       if (t + 2 < n_tiles) copy_tile(t + 2);
       if (t + 3 < n_tiles) copy_tile(t + 3);
-      compute(t, s0);
       if (t + 1 < n_tiles) compute(t + 1, s1);
       wait_vmcnt0();
       __syncthreads();
