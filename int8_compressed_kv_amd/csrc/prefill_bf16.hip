@@ -70,6 +70,11 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
                : "memory", "m0");
 }
+// The same copy addressed as a wave-uniform 64-bit base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 // s_waitcnt vmcnt(0), the other counters unconstrained (gfx9 encoding)
 __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
@@ -340,15 +345,33 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
     const unsigned lds_k0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned short*)&lds_k[0][0];
     const unsigned lds_v0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned short*)&lds_v[0][0];
     const int last_key = a.s_k - 1;
+    // whole tiles: a scalar tile base, a constant per-lane byte offset and scalar LDS segment
+    // addresses, so a copy costs no vector instruction; the last, partial tile clamps its rows
+    unsigned voff[SPW], seg_k[SPW], seg_v[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      voff[j] = 2u * (unsigned)(crow[j] * D + ccol[j]);
+      seg_k[j] = __builtin_amdgcn_readfirstlane(lds_k0 + 1024u * (unsigned)(SPW * wave + j));
+      seg_v[j] = __builtin_amdgcn_readfirstlane(lds_v0 + 1024u * (unsigned)(SPW * wave + j));
+    }
     auto copy_tile = [&](int t) {
       const int k0 = (t_lo + t) * BN;
       const unsigned st_off = 2u * C::TILE * (unsigned)(t % NST);
+      if (k0 + BN <= a.s_k) {
+        const unsigned short* kt = kp + (int64_t)k0 * D;
+        const unsigned short* vt = vp + (int64_t)k0 * D;
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
-        const unsigned seg = st_off + 1024u * (unsigned)(SPW * wave + j);
-        copy16_to_lds(kp + row * D + ccol[j], __builtin_amdgcn_readfirstlane(lds_k0 + seg));
-        copy16_to_lds(vp + row * D + ccol[j], __builtin_amdgcn_readfirstlane(lds_v0 + seg));
+        for (int j = 0; j < SPW; ++j) {
+          copy16_to_lds(kt, voff[j], seg_k[j] + st_off);
+          copy16_to_lds(vt, voff[j], seg_v[j] + st_off);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
+          copy16_to_lds(kp + row * D + ccol[j], seg_k[j] + st_off);
+          copy16_to_lds(vp + row * D + ccol[j], seg_v[j] + st_off);
+        }
       }
     };
     auto pair = [&](int t, auto s0, auto s1) {
