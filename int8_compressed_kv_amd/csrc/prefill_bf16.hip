@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   const int h = lane >> 5;       // half of the wave (MFMA k-slot group)
   const int c = lane & 31;       // MFMA column (query) / row (key, head-dim)
   const int g16 = lane >> 4;     // 16-lane group of the transposing reads
@@ -296,19 +296,24 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
         mc = m_use * c2;
       }
       // P^T as B operands: k-step (kb, s2) takes the exponentials of S[kb][8 s2 .. 8 s2 + 7].  The
-      // row sum is taken over the bf16-rounded P the MFMA multiplies, two values per v_dot2.
+      // row sum adds the fp32 exponentials as a tree (plain adds: v_dot2 does not issue alongside
+      // the matrix pipe), so l, and the LSE, are the exact sums of the exponentials.
       u32x4 Pw[2][2];
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float lpair[16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int q2 = 0; q2 < 8; ++q2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][2 * q2], c2, -mc));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][2 * q2 + 1], c2, -mc));
-          const unsigned w = pack_bf16x2(p0, p1);
-          Pw[kb][q2 / 4][q2 % 4] = w;
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
+          Pw[kb][q2 / 4][q2 % 4] = pack_bf16x2(p0, p1);
+          lpair[kb * 8 + q2] = p0 + p1;
         }
+#pragma unroll
+      for (int st2 = 8; st2 >= 1; st2 >>= 1)
+#pragma unroll
+        for (int j = 0; j < st2; ++j) lpair[j] += lpair[j + st2];
+      l_run += lpair[0];
 
       // O^T[db] += V^T P^T
 #pragma unroll

@@ -29,7 +29,7 @@ def test_gqa_prefill_bf16_reduced_c5(causal, window):
     out, lse = _bf16(q, k, v, causal=causal, window=window, return_lse=True)
     ref, lref = oracle.attention(q, k, v, causal=causal, window=window)
     check_bf16_output(to_np(out), ref, "bf16 out")
-    check_close(to_np(lse), lref, 2e-3, "lse")
+    check_close(to_np(lse), lref, 1e-4, "lse")   # l is the fp32 sum of the fp32 exponentials
     o32 = _bf16(q, k, v, causal=causal, window=window, out_dtype=torch.float32)
     check_close(to_np(o32), ref, TOL_BF16, "fp32 output of the bf16 path")
     assert torch.equal(o32.to(torch.bfloat16), out), "bf16 store is not the RNE of the fp32 result"
