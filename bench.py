@@ -8,6 +8,8 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   c3     int8-KV causal prefill, bf16 Q, 4 x 32 heads, 4096 tokens, d 128, bf16 output
   c4     GQA split-KV decode over the int8 cache, 16 x 32 query / 8 KV heads, 32768 keys, d 128
   comp   per-token compression of the c4 K and V caches (fp32 -> int8 + fp32 scales)
+  append decode-time cache write of the c4 shape: one new fp32 K and V token per KV head (128),
+         quantized into the 32768-row int8 cache at device-held positions (latency-bound)
   copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
          that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to HBM bytes
 
@@ -51,6 +53,7 @@ LEG_SOURCES = {
     "c3": ("prefill_i8kv.hip", "device_common.hpp", "kernel_args.hpp"),
     "c4": ("decode.hip", "device_common.hpp", "kernel_args.hpp"),
     "comp": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
+    "append": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
@@ -114,7 +117,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp")
+    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp,append")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
     args = ap.parse_args()
@@ -187,7 +190,7 @@ def main():
         del qd, kc, ks, vc, vs, out, q, k, v
 
     # ------------------------------------------------------------------ compress + decode c4
-    if legs & {"c4", "comp"}:
+    if legs & {"c4", "comp", "append"}:
         w = WORKLOADS["c4"]
         log(f"[bench] generating {w.name}")
         q, k, v = draw_qkv(w)
@@ -211,6 +214,22 @@ def main():
             log(f"[bench] comp: {avg:.3f} ms  {res['comp']['gbs']:.0f} GB/s")
         fa.compress_kv(kf, kc, ks)
         fa.compress_kv(vf, vc, vs)
+        if "append" in legs:
+            # the cache's last token of every KV head written again from its fp32 values (the
+            # codes written are the ones already there, so the decode leg sees the same cache)
+            kn = kf[:, -1:].contiguous()
+            vn = vf[:, -1:].contiguous()
+            pos = torch.full((w.bh_kv,), w.s_k - 1, dtype=torch.int32, device="cuda")
+            fn = lambda: fa.append_kv(kn, vn, pos, kc, vc, ks, vs)   # noqa: E731
+            log("[bench] timing append (c4 shape, one token per KV head)")
+            ms = timer.run(fn, max(args.steps, 50), args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = 2 * w.bh_kv * (w.d * 4 + w.d + 4) + w.bh_kv * 4
+            res["append"] = {"workload": "append_c4_1tok_kv128_d128_f32", "ms": avg, "ms_min": float(np.min(ms)),
+                             "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
+                             "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS, "bound": "launch latency"}
+            log(f"[bench] append: {avg * 1e3:.1f} us")
+            del kn, vn, pos
         del kf, vf
         out = torch.empty((w.bh_q, 1, w.d), dtype=torch.float32, device="cuda")
         splits = fa.decode_num_splits(w.bh_q, w.bh_kv, w.s_k, w.d)

@@ -12,6 +12,9 @@
  *                      p.v (fkl PR, Summary: flash_attention(), epilogue=[...], layout
  *                      and precision bullet; SKaiNET PR #419, Summary: GQA groups and
  *                      sliding-window layers).
+ *   fa_append_kv    -- the decode-time cache write: new K/V tokens quantized by the
+ *                      same rule into the int8 cache at device-held positions (fkl PR,
+ *                      Summary: the compressed cache holds K/V for long-context decode).
  *   fa_decode       -- one query row per head against an int8 cache, split over the
  *                      keys with a log-sum-exp merge of the partial (m, l, O) states
  *                      (fkl PR, Verification: the decode check; kernbench2 ADR-0060
@@ -81,6 +84,23 @@ typedef struct {
  */
 int fa_compress_kv(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_dim,
                    int8_t* q_out, float* scale_out, void* stream);
+
+/*
+ * fa_append_kv -- quantize n_new new tokens per KV head of K and of V into an int8 cache.
+ *   k_new, v_new     device, [bh_kv, n_new, head_dim], x_dtype FA_F32 or FA_BF16.
+ *   pos              device int32 [bh_kv]: token j of KV head b goes to cache row pos[b] + j.
+ *                    Read on the device, so the call can be replayed (for instance from a
+ *                    captured graph) while the caller advances the positions; different heads
+ *                    (sequences) may sit at different lengths.
+ *   k_cache, v_cache device int8 [bh_kv, capacity, head_dim]; k_scale, v_scale device fp32
+ *                    [bh_kv, capacity].  Rows outside [0, capacity) are skipped, never written.
+ * Codes and scales are bit-identical to fa_compress_kv of the same rows (fkl PR, Summary:
+ * compress_kv(), one fp32 scale per token).  Inputs may not alias the caches.
+ * n_new == 0 is a no-op that returns FA_OK.
+ */
+int fa_append_kv(const void* k_new, const void* v_new, int32_t x_dtype, int32_t bh_kv, int32_t n_new,
+                 int32_t head_dim, const int32_t* pos, int32_t capacity, int8_t* k_cache, int8_t* v_cache,
+                 float* k_scale, float* v_scale, void* stream);
 
 /*
  * fa_forward -- attention forward for bh_q query heads over bh_kv KV heads.

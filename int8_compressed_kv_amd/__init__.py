@@ -10,6 +10,7 @@ present, the calls raise.
     out = flash_attention(q, k, v, causal=True)          # bf16 or fp32
     out = flash_attention(q, kc, vc, k_scale=ks, v_scale=vs, causal=True,
                           epilogue=[Mul(2.0), Add(0.5)])
+    append_kv(k1, v1, pos, kc, vc, ks, vs)               # quantize new tokens into the cache
     out = decode(q1, kc, vc, ks, vs)                     # split-KV decode step
 
 Layout (batch*heads, seq, head_dim), head_dim a multiple of 32 up to 256.
@@ -20,7 +21,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Mul", "Add", "compress_kv", "flash_attention", "decode", "decode_workspace_bytes",
+__all__ = ["Mul", "Add", "compress_kv", "append_kv", "flash_attention", "decode", "decode_workspace_bytes",
            "decode_num_splits", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
            "F32", "BF16", "I8"]
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     L.fa_compress_kv.argtypes = [vp, i32, i64, i32, vp, vp, vp]
     L.fa_compress_kv.restype = ctypes.c_int
+    L.fa_append_kv.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp]
+    L.fa_append_kv.restype = ctypes.c_int
     L.fa_forward.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                              i32, i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(_EpiOp), i32, vp]
     L.fa_forward.restype = ctypes.c_int
@@ -172,6 +175,31 @@ def compress_kv(x, out=None, scales=None):
     _check(lib().fa_compress_kv(_dev(x, "x"), _dtype_code(x), n, d, _dev(out, "codes"),
                                 _dev(scales, "scales"), _stream()))
     return out, scales
+
+
+def append_kv(k_new, v_new, pos, k_cache, v_cache, k_scale, v_scale):
+    """Quantize new tokens k_new, v_new (bh_kv, n_new, d) fp32/bf16 into the int8 cache
+    (bh_kv, capacity, d) with scales (bh_kv, capacity): token j of head b goes to row pos[b] + j,
+    pos an int32 device tensor (bh_kv,).  Rows outside the cache are skipped."""
+    torch = _torch()
+    if k_new.dim() != 3 or tuple(v_new.shape) != tuple(k_new.shape) or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must be (bh_kv, n_new, head_dim) tensors of one dtype")
+    bh_kv, n_new, d = k_new.shape
+    if k_cache.dim() != 3 or k_cache.shape[0] != bh_kv or k_cache.shape[2] != d:
+        raise ValueError("k_cache must be (bh_kv, capacity, head_dim)")
+    cap = k_cache.shape[1]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != torch.int8 or v_cache.dtype != torch.int8:
+        raise ValueError("k_cache and v_cache must be int8 tensors of one shape")
+    if tuple(k_scale.shape) != (bh_kv, cap) or tuple(v_scale.shape) != (bh_kv, cap):
+        raise ValueError("scales must have shape (bh_kv, capacity)")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise ValueError("scales must be fp32")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (bh_kv,):
+        raise ValueError("pos must be an int32 tensor of shape (bh_kv,)")
+    _check(lib().fa_append_kv(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new), bh_kv, n_new, d,
+                              _dev(pos, "pos"), cap, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                              _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream()))
+    return k_cache, v_cache, k_scale, v_scale
 
 
 def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(), k_scale=None,

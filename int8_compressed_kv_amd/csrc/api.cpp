@@ -95,6 +95,41 @@ int fa_compress_kv(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t hea
   return FA_OK;
 }
 
+int fa_append_kv(const void* k_new, const void* v_new, int32_t x_dtype, int32_t bh_kv, int32_t n_new,
+                 int32_t head_dim, const int32_t* pos, int32_t capacity, int8_t* k_cache, int8_t* v_cache,
+                 float* k_scale, float* v_scale, void* stream) {
+  g_last_error.clear();
+  if (int r = check_head_dim(head_dim)) return r;
+  if (x_dtype != FA_F32 && x_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "append_kv input must be FA_F32 or FA_BF16 (got %d)", x_dtype);
+  if (bh_kv <= 0) return fail(FA_ERR_INVALID, "bh_kv must be positive (got %d)", bh_kv);
+  if (n_new < 0) return fail(FA_ERR_INVALID, "n_new must be >= 0 (got %d)", n_new);
+  if (capacity <= 0) return fail(FA_ERR_INVALID, "capacity must be positive (got %d)", capacity);
+  if (n_new == 0) return FA_OK;
+  if (!k_new || !v_new || !pos || !k_cache || !v_cache || !k_scale || !v_scale)
+    return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return fail(FA_ERR_INVALID, "new tokens and caches must be 16-byte aligned, scales and pos 4-byte aligned");
+  fa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pos = pos;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.bh_kv = bh_kv;
+  a.n_new = n_new;
+  a.capacity = capacity;
+  const char* name = "";
+  hipError_t e = fa::launch_append(a, head_dim, x_dtype, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "append_kv launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
 int fa_forward(const void* q, int32_t q_dtype, const void* k, const void* v, int32_t kv_dtype,
                const float* k_scale, const float* v_scale, void* out, int32_t out_dtype, float* lse_out,
                int32_t bh_q, int32_t bh_kv, int32_t s_q, int32_t s_k, int32_t head_dim, float softmax_scale,

@@ -39,6 +39,75 @@ __device__ __forceinline__ float segment_max(float a) {
   return a;
 }
 
+// Codes and scale of one token row held by a segment of SEG lanes, ELEM values per lane (every
+// lane of the segment holds valid values; idle lanes repeat a chunk).  Returns s; packed[] gets
+// the lane's ELEM codes, four per word.
+template <int ELEM, int SEG>
+__device__ __forceinline__ float quantize_row(const float (&x)[ELEM], unsigned (&packed)[ELEM / 4]) {
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < ELEM; ++e) a = fmaxf(a, fabsf(x[e]));
+  a = segment_max<SEG>(a);
+  const float s = __fdiv_rn(a, 127.0f);
+  // code = rint(RN(x / s)) clamped to [-127, 127].  The correctly rounded quotient comes from
+  // the correctly rounded reciprocal y = RN(1 / s) and one correction step (Markstein):
+  // q0 = RN(x y) is within an ulp of x / s, the residual e = x - s q0 is exact in one fma,
+  // and RN(q0 + e y) = RN(x / s).  It needs no over- or underflow, which holds for
+  // s >= 2^-64 (|x / s| <= 127 + 2^-16 here); smaller nonzero scales take the IEEE division.
+  const float y = __fdiv_rn(1.0f, s);
+  float c[ELEM];
+#pragma unroll
+  for (int e = 0; e < ELEM; ++e) {
+    const float q0 = x[e] * y;
+    const float r = __builtin_fmaf(-s, q0, x[e]);
+    c[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(__builtin_fmaf(r, y, q0)), -127.f, 127.f);
+  }
+  if (__builtin_expect(__any(s < 0x1p-64f && s > 0.f), 0)) {
+#pragma unroll
+    for (int e = 0; e < ELEM; ++e)
+      if (s < 0x1p-64f) c[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(__fdiv_rn(x[e], s)), -127.f, 127.f);
+  }
+#pragma unroll
+  for (int e4 = 0; e4 < ELEM / 4; ++e4) {
+    unsigned w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int ci = s > 0.f ? (int)c[4 * e4 + b] : 0;   // an all-zero token: s = 0, codes 0
+      w |= ((unsigned)ci & 0xffu) << (8 * b);
+    }
+    packed[e4] = w;
+  }
+  return s;
+}
+
+// 16 bytes of a row: ELEM values (fp32 x4 or bf16 x8, bf16 widened exactly)
+template <bool BF16_IN, int ELEM>
+__device__ __forceinline__ void load_chunk(const void* p, float (&x)[ELEM]) {
+  if constexpr (BF16_IN) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  } else {
+    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = w[e];
+  }
+}
+
+// the lane's codes of a row at dst (ELEM bytes)
+template <int ELEM>
+__device__ __forceinline__ void store_codes(int8_t* dst, const unsigned (&packed)[ELEM / 4]) {
+  if constexpr (ELEM == 8) {
+    const u32x2 p2 = {packed[0], packed[ELEM / 4 - 1]};
+    __builtin_nontemporal_store(p2, reinterpret_cast<u32x2*>(dst));
+  } else {
+    __builtin_nontemporal_store(packed[0], reinterpret_cast<unsigned*>(dst));
+  }
+}
+
 template <int D, bool BF16_IN, int U>
 __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ xin, int64_t n,
                                                        int8_t* __restrict__ qout,
@@ -65,69 +134,71 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = min(base + (int64_t)u * RPW + sub, n - 1);
-      if (BF16_IN) {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            static_cast<const unsigned short*>(xin) + row * D + chunk * ELEM));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[u][2 * e] = __uint_as_float(w[e] << 16);
-          x[u][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
-      } else {
-        const f32x4 w = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(static_cast<const float*>(xin) + row * D + chunk * ELEM));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[u][e] = w[e];
-      }
+      load_chunk<BF16_IN, ELEM>(static_cast<const char*>(xin) + (row * D + chunk * ELEM) * (BF16_IN ? 2 : 4), x[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float a = 0.f;
-#pragma unroll
-      for (int e = 0; e < ELEM; ++e) a = fmaxf(a, fabsf(x[u][e]));
-      a = segment_max<SEG>(a);
-      const float s = __fdiv_rn(a, 127.0f);
-      // code = rint(RN(x / s)) clamped to [-127, 127].  The correctly rounded quotient comes from
-      // the correctly rounded reciprocal y = RN(1 / s) and one correction step (Markstein):
-      // q0 = RN(x y) is within an ulp of x / s, the residual e = x - s q0 is exact in one fma,
-      // and RN(q0 + e y) = RN(x / s).  It needs no over- or underflow, which holds for
-      // s >= 2^-64 (|x / s| <= 127 + 2^-16 here); smaller nonzero scales take the IEEE division.
-      const float y = __fdiv_rn(1.0f, s);
-      float c[ELEM];
-#pragma unroll
-      for (int e = 0; e < ELEM; ++e) {
-        const float q0 = x[u][e] * y;
-        const float r = __builtin_fmaf(-s, q0, x[u][e]);
-        c[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(__builtin_fmaf(r, y, q0)), -127.f, 127.f);
-      }
-      if (__builtin_expect(__any(s < 0x1p-64f && s > 0.f), 0)) {
-#pragma unroll
-        for (int e = 0; e < ELEM; ++e)
-          if (s < 0x1p-64f) c[e] = __builtin_amdgcn_fmed3f(__builtin_rintf(__fdiv_rn(x[u][e], s)), -127.f, 127.f);
-      }
       unsigned packed[ELEM / 4];
-#pragma unroll
-      for (int e4 = 0; e4 < ELEM / 4; ++e4) {
-        unsigned w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int ci = s > 0.f ? (int)c[4 * e4 + b] : 0;   // an all-zero token: s = 0, codes 0
-          w |= ((unsigned)ci & 0xffu) << (8 * b);
-        }
-        packed[e4] = w;
-      }
+      const float s = quantize_row<ELEM, SEG>(x[u], packed);
       const int64_t row = base + (int64_t)u * RPW + sub;
       if (lane_on && row < n) {
-        if (ELEM == 8) {
-          const u32x2 p2 = {packed[0], packed[ELEM / 4 - 1]};
-          __builtin_nontemporal_store(p2, reinterpret_cast<u32x2*>(qout + row * D + seg_lane * ELEM));
-        } else {
-          __builtin_nontemporal_store(packed[0], reinterpret_cast<unsigned*>(qout + row * D + seg_lane * ELEM));
-        }
+        store_codes<ELEM>(qout + row * D + seg_lane * ELEM, packed);
         if (seg_lane == 0) __builtin_nontemporal_store(s, sout + row);
       }
     }
   }
+}
+
+// Decode-time append: the n_new new tokens of every KV head, of K and of V, quantized exactly as
+// above into cache rows pos[b] + j (positions read on the device, so the call can be replayed
+// at advancing positions; one position per head also covers sequences of different lengths).
+// Global row r covers matrix r / (bh_kv n_new) (K, then V), head b and new token j; rows whose
+// cache position falls outside [0, capacity) are not written.
+template <int D, bool BF16_IN>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int ELEM = BF16_IN ? 8 : 4;
+  constexpr int R = D / ELEM;
+  constexpr int SEG = pow2_at_least(R);
+  constexpr int RPW = 64 / SEG;
+  const int lane = threadIdx.x & 63;
+  const int seg_lane = lane % SEG;
+  const bool lane_on = seg_lane < R;
+  const int64_t per_mat = (int64_t)a.bh_kv * a.n_new;
+  const int64_t total = 2 * per_mat;
+  const int64_t r = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / SEG;
+  // every lane takes part in the row reduction: rows past the end repeat the last row
+  const int64_t re = min(r, total - 1);
+  const bool is_v = re >= per_mat;
+  const int64_t rem = is_v ? re - per_mat : re;
+  const int b = (int)(rem / a.n_new), j = (int)(rem % a.n_new);
+  const int chunk = lane_on ? seg_lane : R - 1;
+  float x[ELEM];
+  load_chunk<BF16_IN, ELEM>(static_cast<const char*>(is_v ? a.v_new : a.k_new) + (rem * D + chunk * ELEM) * (BF16_IN ? 2 : 4), x);
+  unsigned packed[ELEM / 4];
+  const float s = quantize_row<ELEM, SEG>(x, packed);
+  const int p = a.pos[b] + j;
+  if (r < total && lane_on && p >= 0 && p < a.capacity) {
+    const int64_t dst = (int64_t)b * a.capacity + p;
+    store_codes<ELEM>((is_v ? a.v_cache : a.k_cache) + dst * D + seg_lane * ELEM, packed);
+    if (seg_lane == 0) (is_v ? a.v_scale : a.k_scale)[dst] = s;
+  }
+}
+
+template <int D>
+hipError_t launch_append_d(const AppendArgs& a, bool bf16, hipStream_t st, const char** name) {
+  const int elem = bf16 ? 8 : 4;
+  const int64_t rows_per_block = 4 * (64 / pow2_at_least(D / elem));
+  const int64_t total = 2 * (int64_t)a.bh_kv * a.n_new;
+  const int64_t blocks = (total + rows_per_block - 1) / rows_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (bf16) {
+    hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    *name = "append_bf16";
+  } else {
+    hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    *name = "append_f32";
+  }
+  return hipGetLastError();
 }
 
 template <int D>
@@ -165,6 +236,21 @@ hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int
     case 192: return launch_d<192>(x, bf16, n_tokens, q_out, scale_out, stream, name);
     case 224: return launch_d<224>(x, bf16, n_tokens, q_out, scale_out, stream, name);
     case 256: return launch_d<256>(x, bf16, n_tokens, q_out, scale_out, stream, name);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, int32_t d, int32_t x_dtype, hipStream_t stream, const char** name) {
+  const bool bf16 = x_dtype == kBF16;
+  switch (d) {
+    case 32: return launch_append_d<32>(a, bf16, stream, name);
+    case 64: return launch_append_d<64>(a, bf16, stream, name);
+    case 96: return launch_append_d<96>(a, bf16, stream, name);
+    case 128: return launch_append_d<128>(a, bf16, stream, name);
+    case 160: return launch_append_d<160>(a, bf16, stream, name);
+    case 192: return launch_append_d<192>(a, bf16, stream, name);
+    case 224: return launch_append_d<224>(a, bf16, stream, name);
+    case 256: return launch_append_d<256>(a, bf16, stream, name);
     default: return hipErrorInvalidValue;
   }
 }

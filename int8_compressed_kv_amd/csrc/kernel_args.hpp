@@ -55,9 +55,21 @@ struct DecodeArgs {
   EpiArgs epi;
 };
 
+struct AppendArgs {
+  const void* k_new;    // [bh_kv, n_new, d]
+  const void* v_new;
+  const int32_t* pos;   // [bh_kv] cache row of each head's first new token
+  int8_t* k_cache;      // [bh_kv, capacity, d]
+  int8_t* v_cache;
+  float* k_scale;       // [bh_kv, capacity]
+  float* v_scale;
+  int32_t bh_kv, n_new, capacity;
+};
+
 // Launchers return hipSuccess or the launch error; *name receives the instantiation name.
 hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d,
                            int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);
+hipError_t launch_append(const AppendArgs& a, int32_t d, int32_t x_dtype, hipStream_t stream, const char** name);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int32_t d, int32_t kv_dtype, hipStream_t stream,
                               const char** name);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);

@@ -9,12 +9,12 @@ It shares no code, constants or helpers with the HIP path.
 Modules
   attention  -- softmax(Q K^T * scale) V with causal / window / GQA masks, the
                 Mul/Add epilogue, log-sum-exp, dequantization of int8 K/V.
-  quantize   -- the per-token absmax/127 int8 quantizer (numpy fp32) and the
-                closed-form compression ratio.
+  quantize   -- the per-token absmax/127 int8 quantizer (numpy fp32), the
+                closed-form compression ratio and the decode-time cache write.
 
 Every function is pinned by tests in tests/test_oracle_pins.py (brute force,
 a library cross-check, invariants and closed forms).  No function here is
 "parity unpinned".
 """
 from .attention import attention, apply_epilogue, dequantize, visible_mask, decode  # noqa: F401
-from .quantize import quantize_per_token, compression_ratio  # noqa: F401
+from .quantize import quantize_per_token, compression_ratio, append_kv  # noqa: F401

@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["quantize_per_token", "compression_ratio"]
+__all__ = ["quantize_per_token", "compression_ratio", "append_kv"]
 
 
 def quantize_per_token(x) -> tuple[np.ndarray, np.ndarray]:
@@ -44,3 +44,24 @@ def quantize_per_token(x) -> tuple[np.ndarray, np.ndarray]:
 def compression_ratio(head_dim: int, src_bytes_per_elem: int = 4) -> float:
     """Bytes of an uncompressed token over bytes of its int8 codes + one fp32 scale."""
     return (src_bytes_per_elem * head_dim) / (head_dim + 4)
+
+
+def append_kv(k_cache, v_cache, k_scale, v_scale, k_new, v_new, pos):
+    """Decode-time cache write, on copies of the caches: token j of KV head b (of k_new and
+    v_new, (bh_kv, n_new, d)) is quantized as above and stored at row pos[b] + j of its head;
+    rows outside [0, capacity) are skipped.  The pages keep the compressed cache for long-context
+    decode (fkl PR, Summary); placing each new token at its position is the plain reading.
+    Returns (k_cache, v_cache, k_scale, v_scale) as new arrays."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    ks, vs = np.array(k_scale, copy=True), np.array(v_scale, copy=True)
+    cap = kc.shape[1]
+    for b in range(k_new.shape[0]):
+        for j in range(k_new.shape[1]):
+            p = int(pos[b]) + j
+            if not 0 <= p < cap:
+                continue
+            for new, codes, scales in ((k_new, kc, ks), (v_new, vc, vs)):
+                q, s = quantize_per_token(new[b, j])
+                codes[b, p] = q
+                scales[b, p] = s
+    return kc, vc, ks, vs

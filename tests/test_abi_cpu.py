@@ -28,7 +28,7 @@ def L():
 
 def test_header_declares_the_three_operations():
     names = _header_functions()
-    for n in ("fa_compress_kv", "fa_forward", "fa_decode", "fa_decode_workspace_bytes",
+    for n in ("fa_compress_kv", "fa_append_kv", "fa_forward", "fa_decode", "fa_decode_workspace_bytes",
               "fa_decode_num_splits", "fa_last_error", "fa_last_kernel", "fa_version"):
         assert n in names
 
@@ -133,3 +133,26 @@ def test_python_layer_validates_shapes():
         fa._epilogue([("mul", 2.0)])
     with pytest.raises(ValueError):
         fa._epilogue([fa.Mul(1.0)] * 9)
+
+
+def _app(L, **kw):
+    a = dict(kn=1 << 20, vn=1 << 20, xd=0, bh=4, n=1, d=128, pos=1 << 20, cap=100, kc=1 << 20, vc=1 << 20,
+             ks=1 << 20, vs=1 << 20)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.fa_append_kv(vp(a["kn"]), vp(a["vn"]), a["xd"], a["bh"], a["n"], a["d"], vp(a["pos"]), a["cap"],
+                          vp(a["kc"]), vp(a["vc"]), vp(a["ks"]), vp(a["vs"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=40), -2), (dict(xd=2), -2), (dict(bh=0), -1), (dict(n=-1), -1), (dict(cap=0), -1),
+    (dict(pos=0), -1), (dict(kc=0), -1), (dict(vs=0), -1), (dict(kn=(1 << 20) + 8), -1),
+    (dict(ks=(1 << 20) + 2), -1),
+])
+def test_append_rejects_invalid_arguments_on_host(L, kw, code):
+    rc = _app(L, **kw)
+    assert rc == code, (rc, fa.last_error())
+
+
+def test_append_zero_tokens_is_a_noop(L):
+    assert _app(L, n=0, kn=0, vn=0, pos=0, kc=0, vc=0, ks=0, vs=0) == 0

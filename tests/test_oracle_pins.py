@@ -359,3 +359,40 @@ def test_quantization_error_is_bounded_like_the_pages_claim():
     o_q, _ = oracle.decode(q, kq, vq, k_scale=ks, v_scale=vs)
     err = np.abs(o_ref - o_q).max()
     assert 1e-4 < err < 1e-2
+
+
+def test_append_kv_hand_placement():
+    """Placement of new tokens at device-held positions, against a hand-worked fixture."""
+    g = json.load(open(os.path.join(GOLDEN, "append_placement.json")))
+    kn = np.array(g["k_new"], np.float32)
+    bh, cap, d = kn.shape[0], g["capacity"], kn.shape[2]
+    kc = np.full((bh, cap, d), g["cache_before_fill"], np.int8)
+    ks = np.full((bh, cap), g["scale_before_fill"], np.float32)
+    kc2, vc2, ks2, vs2 = oracle.append_kv(kc, kc, ks, ks, kn, -kn, np.array(g["pos"]))
+    assert kc2.tolist() == g["expected_codes"]
+    want_s = np.array(g["expected_scales_times_127"], np.float64) / 127
+    assert np.all(np.abs(ks2.astype(np.float64) - want_s) <= 1e-7 * np.maximum(want_s, 1e-30))
+    # V carries the negated tokens: codes negate, scales agree
+    assert np.array_equal(vc2[ks2 != ks], -kc2[ks2 != ks]) and np.array_equal(vs2, ks2)
+    # the inputs were not modified in place
+    assert np.all(kc == g["cache_before_fill"])
+
+
+def test_append_kv_token_by_token_equals_whole_sequence_quantization():
+    """Writing a sequence one token per step, at advancing positions, gives exactly the codes and
+    scales of quantizing the whole sequence at once (each token is quantized on its own)."""
+    k, v = rng_normal(35, (3, 9, 32), (3, 9, 32))
+    kc = np.zeros((3, 12, 32), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((3, 12), np.float32)
+    vs = np.zeros_like(ks)
+    start = np.array([0, 2, 3])
+    for j in range(9):
+        kc, vc, ks, vs = oracle.append_kv(kc, vc, ks, vs, k[:, j:j + 1], v[:, j:j + 1], start + j)
+    kq, ksq = oracle.quantize_per_token(k)
+    vq, vsq = oracle.quantize_per_token(v)
+    for b in range(3):
+        n = min(9, 12 - start[b])
+        assert np.array_equal(kc[b, start[b]:start[b] + n], kq[b, :n])
+        assert np.array_equal(vs[b, start[b]:start[b] + n], vsq[b, :n])
+        assert np.all(kc[b, :start[b]] == 0) and np.all(ks[b, :start[b]] == 0)
