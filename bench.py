@@ -10,6 +10,8 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   comp   per-token compression of the c4 K and V caches (fp32 -> int8 + fp32 scales)
   append decode-time cache write of the c4 shape: one new fp32 K and V token per KV head (128),
          quantized into the 32768-row int8 cache at device-held positions (latency-bound)
+  merge  log-sum-exp merge of 8 key-chunk results for one 4096-row query chunk of the c5 shape
+         (64 heads x 4096 rows, d 128, fp32 parts, bf16 output): the exchange of a ring prefill
   copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
          that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to HBM bytes
 
@@ -54,6 +56,7 @@ LEG_SOURCES = {
     "c4": ("decode.hip", "device_common.hpp", "kernel_args.hpp"),
     "comp": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
     "append": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
+    "merge": ("merge.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
@@ -117,7 +120,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp,append")
+    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp,append,merge")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
     args = ap.parse_args()
@@ -248,6 +251,24 @@ def main():
             if not args.no_cpu:
                 cpu["c4"] = decode_cpu_baseline(q, kc, ks, vc, vs, out, w, args.cpu_seconds)
         del qd, kc, vc, ks, vs, out, ws
+
+    if "merge" in legs:
+        n_parts, rows, d = 8, 64 * 4096, 128
+        g = torch.Generator(device="cuda")
+        g.manual_seed(9)
+        o_parts = torch.randn((n_parts, rows, d), generator=g, device="cuda", dtype=torch.float32)
+        lse_parts = torch.randn((n_parts, rows), generator=g, device="cuda", dtype=torch.float32) * 4
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: fa.merge_lse(o_parts, lse_parts, out=out)   # noqa: E731
+        log("[bench] timing merge (8 parts x 64 heads x 4096 rows, d 128)")
+        ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+        avg = float(np.mean(ms))
+        nbytes = n_parts * rows * (d * 4 + 4) + rows * d * 2
+        res["merge"] = {"workload": "merge_8parts_h64_4096rows_d128_f32_to_bf16", "ms": avg,
+                        "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "bytes_per_launch": nbytes,
+                        "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+        log(f"[bench] merge: {avg * 1e3:.1f} us  {res['merge']['gbs']:.0f} GB/s")
+        del o_parts, lse_parts, out
 
     if "copy" in legs:
         src = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")

@@ -15,6 +15,10 @@
  *   fa_append_kv    -- the decode-time cache write: new K/V tokens quantized by the
  *                      same rule into the int8 cache at device-held positions (fkl PR,
  *                      Summary: the compressed cache holds K/V for long-context decode).
+ *   fa_merge_lse    -- exact attention over a union of key chunks from the chunks'
+ *                      normalised outputs and log-sum-exps, the state a split or ring
+ *                      prefill exchanges (kernbench2 ADR-0060 commit: partial (m, l, O)
+ *                      states reduced into one).
  *   fa_decode       -- one query row per head against an int8 cache, split over the
  *                      keys with a log-sum-exp merge of the partial (m, l, O) states
  *                      (fkl PR, Verification: the decode check; kernbench2 ADR-0060
@@ -123,6 +127,27 @@ int fa_forward(const void* q, int32_t q_dtype,
                int32_t bh_q, int32_t bh_kv, int32_t s_q, int32_t s_k, int32_t head_dim,
                float softmax_scale, int32_t causal, int32_t window,
                const fa_epilogue_op* epi, int32_t n_epi, void* stream);
+
+/*
+ * fa_merge_lse -- merge n_parts attention results for the same `rows` query rows, each over
+ * its own disjoint set of keys, into the result over all of them.
+ *   o_parts    device fp32 [n_parts, rows, head_dim]: each part's normalised output, as
+ *              fa_forward writes it with out_dtype FA_F32 and no epilogue.
+ *   lse_parts  device fp32 [n_parts, rows]: each part's log-sum-exp (fa_forward's lse_out;
+ *              -inf for a row with no visible key in that part).
+ *   out        device [rows, head_dim], out_dtype FA_F32 or FA_BF16 (RNE cast).
+ *   lse_out    device or NULL, [rows] fp32.
+ *   epi, n_epi the Mul/Add epilogue, applied once to the merged row before the cast.
+ * LSE = log sum_p exp(LSE_p); out = sum_p exp(LSE_p - LSE) O_p, computed against the largest
+ * LSE_p; a row with every LSE_p = -inf gives 0 and -inf.  With the keys split into chunks
+ * aligned with chunks of the queries, each (query chunk, key chunk) part is either fully
+ * visible, a causal diagonal block, or empty, so a causal prefill splits into fa_forward calls
+ * and one merge (the exchange of a ring / context-parallel prefill).
+ * rows == 0 is a no-op.  out may not alias the inputs.
+ */
+int fa_merge_lse(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows, int32_t head_dim,
+                 void* out, int32_t out_dtype, float* lse_out, const fa_epilogue_op* epi, int32_t n_epi,
+                 void* stream);
 
 /*
  * fa_decode_num_splits -- the split count fa_decode uses when num_splits == 0.

@@ -12,6 +12,7 @@ present, the calls raise.
                           epilogue=[Mul(2.0), Add(0.5)])
     append_kv(k1, v1, pos, kc, vc, ks, vs)               # quantize new tokens into the cache
     out = decode(q1, kc, vc, ks, vs)                     # split-KV decode step
+    out = merge_lse(o_parts, lse_parts)                  # attention over a union of key chunks
 
 Layout (batch*heads, seq, head_dim), head_dim a multiple of 32 up to 256.
 """
@@ -21,7 +22,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Mul", "Add", "compress_kv", "append_kv", "flash_attention", "decode", "decode_workspace_bytes",
+__all__ = ["Mul", "Add", "compress_kv", "append_kv", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
            "decode_num_splits", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
            "F32", "BF16", "I8"]
 
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.fa_forward.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                              i32, i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(_EpiOp), i32, vp]
     L.fa_forward.restype = ctypes.c_int
+    L.fa_merge_lse.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp, ctypes.POINTER(_EpiOp), i32, vp]
+    L.fa_merge_lse.restype = ctypes.c_int
     L.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
     L.fa_decode_num_splits.restype = i32
     L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -232,6 +235,30 @@ def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(),
                             _out_code(out.dtype), _dev(lse, "lse"), bh_q, bh_kv, s_q, s_k, d,
                             float(scale) if scale else 0.0, int(bool(causal)), int(window), epi, n_epi,
                             _stream()))
+    return (out, lse) if return_lse else out
+
+
+def merge_lse(o_parts, lse_parts, *, epilogue=(), out_dtype=None, out=None, return_lse=False):
+    """Attention over the union of disjoint key chunks from per-chunk results: o_parts
+    (n_parts, ..., head_dim) fp32 normalised outputs and lse_parts (n_parts, ...) fp32
+    log-sum-exps, as flash_attention(..., out_dtype=float32, return_lse=True) returns them.
+    Returns out (..., head_dim), or (out, lse) with return_lse."""
+    torch = _torch()
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts and lse_parts must be fp32")
+    if o_parts.dim() < 2 or tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
+        raise ValueError("lse_parts must have the shape of o_parts without its last dimension")
+    n_parts, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel() if n_parts else 0
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(tuple(o_parts.shape[1:]), dtype=odt, device=o_parts.device)
+    if tuple(out.shape) != tuple(o_parts.shape[1:]):
+        raise ValueError("out must have the shape of one part")
+    lse = torch.empty(tuple(lse_parts.shape[1:]), dtype=torch.float32, device=o_parts.device) if return_lse else None
+    epi, n_epi = _epilogue(epilogue)
+    _check(lib().fa_merge_lse(_dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts"), n_parts, rows, d,
+                              _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"), epi, n_epi, _stream()))
     return (out, lse) if return_lse else out
 
 

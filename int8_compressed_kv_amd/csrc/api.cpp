@@ -196,6 +196,37 @@ int fa_forward(const void* q, int32_t q_dtype, const void* k, const void* v, int
   return FA_OK;
 }
 
+int fa_merge_lse(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows, int32_t head_dim,
+                 void* out, int32_t out_dtype, float* lse_out, const fa_epilogue_op* epi, int32_t n_epi,
+                 void* stream) {
+  g_last_error.clear();
+  if (int r = check_head_dim(head_dim)) return r;
+  if (n_parts <= 0) return fail(FA_ERR_INVALID, "n_parts must be positive (got %d)", n_parts);
+  if (rows < 0) return fail(FA_ERR_INVALID, "rows must be >= 0");
+  if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "out dtype must be FA_F32 or FA_BF16");
+  fa::EpiArgs ea;
+  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  if (rows == 0) return FA_OK;
+  if (!o_parts || !lse_parts || !out) return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(o_parts) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse_parts) & 3u) ||
+      (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)))
+    return fail(FA_ERR_INVALID, "o_parts and out must be 16-byte aligned, lse arrays 4-byte aligned");
+  fa::MergeArgs a;
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.out = out;
+  a.lse = lse_out;
+  a.rows = rows;
+  a.n_parts = n_parts;
+  a.out_bf16 = out_dtype == FA_BF16;
+  a.epi = ea;
+  const char* name = "";
+  hipError_t e = fa::launch_merge(a, head_dim, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
 int32_t fa_decode_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim) {
   (void)head_dim;
   if (bh_kv <= 0 || bh_q <= 0 || s_k <= 0) return 1;

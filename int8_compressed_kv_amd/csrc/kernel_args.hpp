@@ -66,6 +66,17 @@ struct AppendArgs {
   int32_t bh_kv, n_new, capacity;
 };
 
+struct MergeArgs {
+  const float* o_parts;   // [n_parts, rows, d] normalised outputs
+  const float* lse_parts; // [n_parts, rows]
+  void* out;              // [rows, d]
+  float* lse;             // [rows] or null
+  int64_t rows;
+  int32_t n_parts;
+  int32_t out_bf16;
+  EpiArgs epi;
+};
+
 // Launchers return hipSuccess or the launch error; *name receives the instantiation name.
 hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d,
                            int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);
@@ -75,5 +86,6 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int32_t d, int32_t kv_dtype,
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_prefill_i8kv(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, const char** name);
+hipError_t launch_merge(const MergeArgs& a, int32_t d, hipStream_t stream, const char** name);
 
 }  // namespace fa

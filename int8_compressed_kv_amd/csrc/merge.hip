@@ -1,0 +1,99 @@
+// Merge of attention outputs computed over disjoint sets of keys, by their log-sum-exp.
+//
+// A split or ring prefill computes, for the same query rows, one normalised output O_p and one
+// log-sum-exp LSE_p per key chunk p (kernbench2 ADR-0060 commit: partial running (m, l, O)
+// states reduced into one; Foundry attention/ README, References: the online-softmax
+// recurrence, whose merge of two states is this one).  Exact attention over the union is
+//   LSE = log sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p,
+// evaluated against M = max_p LSE_p for range: w_p = exp(LSE_p - M), L = sum_p w_p,
+// O = (sum_p w_p O_p) / L, LSE = M + log L.  Chunks with no visible key (LSE_p = -inf, O_p = 0)
+// get weight 0; a row that no chunk covers returns 0 and LSE = -inf, like an empty row of the
+// forward.  The Mul/Add epilogue runs on the merged row, before the cast.
+//
+// HBM-bound: a segment of D/4 lanes owns a row, each lane reading 16 contiguous bytes of every
+// part (nontemporal: each byte is read once), four parts' loads in flight at a time.
+#include "device_common.hpp"
+
+namespace fa {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int SEG = D / 4;     // lanes per row
+  constexpr int RPW = 64 / SEG;  // rows per wave (D <= 256, so SEG <= 64)
+  static_assert(D % 32 == 0 && SEG <= 64, "head_dim must be a multiple of 32, at most 256");
+  const int lane = threadIdx.x & 63;
+  const int sl = lane % SEG;
+  const int64_t row = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / SEG;
+  if (row >= a.rows) return;     // rows are independent: no lane exchange below
+  const float* lse = a.lse_parts + row;
+  float m = neg_inf();
+  for (int p = 0; p < a.n_parts; ++p) m = fmaxf(m, lse[(int64_t)p * a.rows]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  const float mm = m == neg_inf() ? 0.f : m;   // every weight is then 0 for an uncovered row
+  const float* src = a.o_parts + row * D + 4 * sl;
+  // a part of weight 0 adds nothing even if its row holds garbage (select, not multiply)
+  auto add_part = [&](float lp, const f32x4& x) {
+    const float w = __builtin_amdgcn_exp2f((lp - mm) * 1.4426950408889634f);
+    l += w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = w > 0.f ? __builtin_fmaf(w, x[e], acc[e]) : acc[e];
+  };
+  int p = 0;
+  for (; p + 4 <= a.n_parts; p += 4) {   // four parts' loads in flight together
+    float lp[4];
+    f32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lp[u] = lse[(int64_t)(p + u) * a.rows];
+      x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (int64_t)(p + u) * a.rows * D));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add_part(lp[u], x[u]);
+  }
+  for (; p < a.n_parts; ++p)
+    add_part(lse[(int64_t)p * a.rows],
+             __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (int64_t)p * a.rows * D)));
+  const float inv = l > 0.f ? __fdiv_rn(1.0f, l) : 0.f;
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = acc[e] * inv;
+  apply_epilogue_all(y, a.epi);
+  if (a.out_bf16) {
+    const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + 4 * sl) = w;
+  } else {
+    const f32x4 w = {y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + 4 * sl) = w;
+  }
+  if (a.lse && sl == 0) a.lse[row] = l > 0.f ? m + logf(l) : neg_inf();
+}
+
+template <int D>
+hipError_t launch_d(const MergeArgs& a, hipStream_t st, const char** name) {
+  constexpr int rows_per_block = 4 * (64 / (D / 4));
+  const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  *name = "merge_lse";
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int32_t d, hipStream_t stream, const char** name) {
+  switch (d) {
+    case 32: return launch_d<32>(a, stream, name);
+    case 64: return launch_d<64>(a, stream, name);
+    case 96: return launch_d<96>(a, stream, name);
+    case 128: return launch_d<128>(a, stream, name);
+    case 160: return launch_d<160>(a, stream, name);
+    case 192: return launch_d<192>(a, stream, name);
+    case 224: return launch_d<224>(a, stream, name);
+    case 256: return launch_d<256>(a, stream, name);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

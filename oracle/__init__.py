@@ -8,7 +8,8 @@ It shares no code, constants or helpers with the HIP path.
 
 Modules
   attention  -- softmax(Q K^T * scale) V with causal / window / GQA masks, the
-                Mul/Add epilogue, log-sum-exp, dequantization of int8 K/V.
+                Mul/Add epilogue, log-sum-exp, dequantization of int8 K/V, and
+                the merge of results over disjoint key sets by log-sum-exp.
   quantize   -- the per-token absmax/127 int8 quantizer (numpy fp32), the
                 closed-form compression ratio and the decode-time cache write.
 
@@ -16,5 +17,5 @@ Every function is pinned by tests in tests/test_oracle_pins.py (brute force,
 a library cross-check, invariants and closed forms).  No function here is
 "parity unpinned".
 """
-from .attention import attention, apply_epilogue, dequantize, visible_mask, decode  # noqa: F401
+from .attention import attention, apply_epilogue, dequantize, visible_mask, decode, merge_lse  # noqa: F401
 from .quantize import quantize_per_token, compression_ratio, append_kv  # noqa: F401

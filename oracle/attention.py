@@ -28,6 +28,10 @@ What is computed, and where it is defined:
 * The epilogue list runs on the attention output, in list order, after the
   softmax normalisation -- fkl PR, Summary (epilogue=[Mul(2.0), Add(0.5)],
   applied to the attention output inside the kernel).
+* Merging results over disjoint key sets (merge_lse): the partial running states
+  reduced into one -- kernbench2 ADR-0060 commit (split decode / ring prefill
+  with a reduce of the running (m, l, O) states); written here in the plain
+  log-sum-exp form: LSE = log sum_p exp(LSE_p), O = sum_p exp(LSE_p - LSE) O_p.
 * int8 K/V enter as their dequantized values q * s (one fp32 scale per token)
   -- fkl PR, Summary (compress_kv) and the Verification row that compares the
   int8-KV kernel with an oracle fed the dequantized cache.
@@ -36,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["dequantize", "visible_mask", "attention", "apply_epilogue", "decode"]
+__all__ = ["dequantize", "visible_mask", "attention", "apply_epilogue", "decode", "merge_lse"]
 
 ROW_BLOCK = 256  # rows of the score matrix materialised at once (memory bound only)
 
@@ -155,3 +159,26 @@ def decode(q, k, v, *, window: int = 0, scale: float | None = None, epilogue=(),
         raise ValueError("decode expects q of shape (bh_q, 1, d)")
     return attention(q, k, v, causal=True, window=window, scale=scale, epilogue=epilogue,
                      k_scale=k_scale, v_scale=v_scale, heads=heads)
+
+
+def merge_lse(o_parts, lse_parts, epilogue=()):
+    """Attention over the union of disjoint key sets from per-set results, in fp64.
+
+    o_parts: (n_parts, ..., d) normalised outputs; lse_parts: (n_parts, ...) natural-log
+    log-sum-exps (-inf where a set has no visible key).  Softmax over the union weights set p by
+    its share of the total exponential mass, exp(LSE_p) / sum_q exp(LSE_q) (kernbench2 ADR-0060
+    commit: reduce of the running (m, l, O) states).  A row no set covers gives 0 and -inf.
+    The epilogue runs once on the merged row.  Returns (out, lse).
+    """
+    o = np.asarray(o_parts, dtype=np.float64)
+    l = np.asarray(lse_parts, dtype=np.float64)
+    m = l.max(axis=0)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(l - m_safe[None])                          # exp(-inf) = 0 for empty sets
+    tot = w.sum(axis=0)
+    tot_safe = np.where(tot > 0, tot, 1.0)
+    out = (w[..., None] * np.where(np.isneginf(l)[..., None], 0.0, o)).sum(axis=0) / tot_safe[..., None]
+    out[empty] = 0.0
+    lse = np.where(empty, -np.inf, m_safe + np.log(tot_safe))
+    return apply_epilogue(out, epilogue), lse

@@ -28,7 +28,7 @@ def L():
 
 def test_header_declares_the_three_operations():
     names = _header_functions()
-    for n in ("fa_compress_kv", "fa_append_kv", "fa_forward", "fa_decode", "fa_decode_workspace_bytes",
+    for n in ("fa_compress_kv", "fa_append_kv", "fa_forward", "fa_merge_lse", "fa_decode", "fa_decode_workspace_bytes",
               "fa_decode_num_splits", "fa_last_error", "fa_last_kernel", "fa_version"):
         assert n in names
 
@@ -156,3 +156,24 @@ def test_append_rejects_invalid_arguments_on_host(L, kw, code):
 
 def test_append_zero_tokens_is_a_noop(L):
     assert _app(L, n=0, kn=0, vn=0, pos=0, kc=0, vc=0, ks=0, vs=0) == 0
+
+
+def _mrg(L, **kw):
+    a = dict(o=1 << 20, l=1 << 20, n=2, rows=10, d=64, out=1 << 20, od=0, lse=None, epi=None, n_epi=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.fa_merge_lse(vp(a["o"]), vp(a["l"]), a["n"], a["rows"], a["d"], vp(a["out"]), a["od"], vp(a["lse"]),
+                          a["epi"], a["n_epi"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=50), -2), (dict(n=0), -1), (dict(rows=-1), -1), (dict(od=2), -2), (dict(o=0), -1),
+    (dict(out=(1 << 20) + 8), -1), (dict(l=(1 << 20) + 2), -1), (dict(n_epi=9), -2),
+])
+def test_merge_rejects_invalid_arguments_on_host(L, kw, code):
+    rc = _mrg(L, **kw)
+    assert rc == code, (rc, fa.last_error())
+
+
+def test_merge_zero_rows_is_a_noop(L):
+    assert _mrg(L, rows=0, o=0, l=0, out=0) == 0

@@ -396,3 +396,58 @@ def test_append_kv_token_by_token_equals_whole_sequence_quantization():
         assert np.array_equal(kc[b, start[b]:start[b] + n], kq[b, :n])
         assert np.array_equal(vs[b, start[b]:start[b] + n], vsq[b, :n])
         assert np.all(kc[b, :start[b]] == 0) and np.all(ks[b, :start[b]] == 0)
+
+
+def _key_chunks_causal(q, k, v, bounds):
+    """Per-chunk oracle results of a causal prefill with query and key chunks aligned: the block
+    (query chunk r, key chunk c) is full for c < r, causal for c == r, empty for c > r."""
+    outs, lses = [], []
+    for r, (r0, r1) in enumerate(bounds):
+        oo, ll = [], []
+        for c, (c0, c1) in enumerate(bounds):
+            if c > r:
+                oo.append(np.zeros((q.shape[0], r1 - r0, q.shape[2])))
+                ll.append(np.full((q.shape[0], r1 - r0), -np.inf))
+                continue
+            o, l = oracle.attention(q[:, r0:r1], k[:, c0:c1], v[:, c0:c1], causal=(c == r),
+                                    scale=1 / np.sqrt(q.shape[2]))
+            oo.append(o)
+            ll.append(l)
+        outs.append(np.stack(oo))
+        lses.append(np.stack(ll))
+    return outs, lses
+
+
+def test_merge_of_key_chunks_equals_attention_over_all_keys():
+    """Exact attention is a mass-weighted mix of attention over any partition of its keys: the
+    merge of per-chunk results equals the one-shot oracle (an identity of the softmax, checked
+    here against the unsplit computation, causal with aligned query/key chunks, GQA)."""
+    q, k, v = rng_normal(37, (4, 96, 32), (2, 96, 32), (2, 96, 32))
+    bounds = [(0, 17), (17, 40), (40, 41), (41, 96)]
+    full, lfull = oracle.attention(q, k, v, causal=True)
+    outs, lses = _key_chunks_causal(q, k, v, bounds)
+    for (r0, r1), o_p, l_p in zip(bounds, outs, lses):
+        o, l = oracle.merge_lse(o_p, l_p)
+        assert np.abs(o - full[:, r0:r1]).max() < 1e-12
+        assert np.abs(l - lfull[:, r0:r1]).max() < 1e-12
+    # non-causal, keys split in two: the same identity
+    o1, l1 = oracle.attention(q, k[:, :50], v[:, :50], causal=False)
+    o2, l2 = oracle.attention(q, k[:, 50:], v[:, 50:], causal=False)
+    om, lm = oracle.merge_lse(np.stack([o1, o2]), np.stack([l1, l2]), epilogue=[("mul", 2.0), ("add", 0.5)])
+    ref, lref = oracle.attention(q, k, v, causal=False, epilogue=[("mul", 2.0), ("add", 0.5)])
+    assert np.abs(om - ref).max() < 1e-12 and np.abs(lm - lref).max() < 1e-12
+
+
+def test_merge_special_cases():
+    o = rng_normal(38, (3, 5, 8))[0].astype(np.float64)
+    lse = np.array([[0.5, -np.inf, 2.0, 1.0, -np.inf],
+                    [0.5, -np.inf, -np.inf, 1.0, 3.0],
+                    [-np.inf, -np.inf, -np.inf, 1.0, -np.inf]])
+    o[np.isneginf(lse)] = 0.0
+    out, l = oracle.merge_lse(o, lse)
+    # equal masses average; a lone part passes through; no part -> 0 and -inf
+    assert np.allclose(out[0], (o[0, 0] + o[1, 0]) / 2, atol=1e-15) and np.isclose(l[0], 0.5 + np.log(2))
+    assert np.isneginf(l[1]) and np.all(out[1] == 0)
+    assert np.allclose(out[2], o[0, 2], atol=1e-15) and l[2] == 2.0
+    assert np.allclose(out[3], o.mean(axis=0)[3], atol=1e-15) and np.isclose(l[3], 1.0 + np.log(3))
+    assert np.allclose(out[4], o[1, 4], atol=1e-15) and l[4] == 3.0   # parts 0 and 2 empty
