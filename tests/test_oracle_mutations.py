@@ -114,3 +114,61 @@ def test_truncating_quantizer_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "quantize_per_token", _quantizer_variant(np.trunc))
     with pytest.raises(AssertionError):
         pin2()
+
+
+def test_append_position_off_by_one_is_caught(monkeypatch):
+    from test_oracle_pins import test_append_kv_hand_placement as pin
+    pin()
+    oq = importlib.import_module("oracle.quantize")
+    orig = oq.append_kv
+    monkeypatch.setattr(oracle, "append_kv",
+                        lambda kc, vc, ks, vs, kn, vn, pos: orig(kc, vc, ks, vs, kn, vn, np.asarray(pos) + 1))
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_append_writing_past_the_cache_end_is_caught(monkeypatch):
+    """A cache write that wraps a row past the end around to row 0 instead of skipping it."""
+    from test_oracle_pins import test_append_kv_hand_placement as pin
+    oq = importlib.import_module("oracle.quantize")
+
+    def wrapping(kc, vc, ks, vs, kn, vn, pos):
+        kc, vc, ks, vs = (np.array(a, copy=True) for a in (kc, vc, ks, vs))
+        cap = kc.shape[1]
+        for b in range(kn.shape[0]):
+            for j in range(kn.shape[1]):
+                p = (int(pos[b]) + j) % cap
+                for new, codes, scales in ((kn, kc, ks), (vn, vc, vs)):
+                    codes[b, p], scales[b, p] = oq.quantize_per_token(new[b, j])
+        return kc, vc, ks, vs
+    monkeypatch.setattr(oracle, "append_kv", wrapping)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_merge_without_mass_weights_is_caught(monkeypatch):
+    """Averaging the chunk outputs (ignoring each chunk's share of the softmax mass)."""
+    from test_oracle_pins import test_merge_of_key_chunks_equals_attention_over_all_keys as pin
+    pin()
+    orig = oatt.merge_lse
+
+    def plain_mean(o_parts, lse_parts, epilogue=()):
+        o, l = orig(o_parts, lse_parts, epilogue)
+        live = ~np.isneginf(np.asarray(lse_parts))
+        mean = (np.asarray(o_parts) * live[..., None]).sum(0) / np.maximum(live.sum(0), 1)[..., None]
+        return oatt.apply_epilogue(mean, epilogue), l
+    monkeypatch.setattr(oracle, "merge_lse", plain_mean)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_merge_with_max_instead_of_logsumexp_is_caught(monkeypatch):
+    from test_oracle_pins import test_merge_special_cases as pin
+    orig = oatt.merge_lse
+
+    def max_lse(o_parts, lse_parts, epilogue=()):
+        o, _ = orig(o_parts, lse_parts, epilogue)
+        return o, np.asarray(lse_parts, np.float64).max(axis=0)
+    monkeypatch.setattr(oracle, "merge_lse", max_lse)
+    with pytest.raises(AssertionError):
+        pin()
