@@ -63,15 +63,22 @@ typedef enum {
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_I8 = 2 } fa_dtype;
 
-typedef enum { FA_EPI_MUL = 1, FA_EPI_ADD = 2 } fa_epi_kind;
+typedef enum { FA_EPI_MUL = 1, FA_EPI_ADD = 2, FA_EPI_BIAS = 3, FA_EPI_RELU = 4 } fa_epi_kind;
 
 /* One epilogue post-op, applied in fp32 to the normalised attention output, in list order,
- * before the cast to the output dtype (fkl PR, Summary: epilogue=[Mul(2.0), Add(0.5)]).
- * Values and the list itself are kernel arguments: changing either never selects another
- * kernel (fkl PR, Verification: epilogue values change without recompile). */
+ * before the cast to the output dtype (fkl PR, Summary: epilogue=[Mul(2.0), Add(0.5)] -- any
+ * compute ops chained on the output; kernbench2 commit page, the commit that gives
+ * tl.composite() an ordered epilogue list of bias, relu and scale ops).  Each op is one separately rounded IEEE fp32 operation:
+ *   FA_EPI_MUL   x * value            FA_EPI_ADD   x + value
+ *   FA_EPI_BIAS  x + vec[c], c the head-dim index of the element; vec is a device fp32 array
+ *                of head_dim values (4-byte aligned), required for this kind and NULL otherwise
+ *   FA_EPI_RELU  x > 0 ? x : +0 (value unused)
+ * Values, vectors and the list itself are kernel arguments: changing any of them never selects
+ * another kernel (fkl PR, Verification: epilogue values change without recompile). */
 typedef struct {
-  int32_t kind;   /* fa_epi_kind */
-  float value;
+  int32_t kind;        /* fa_epi_kind */
+  float value;         /* FA_EPI_MUL / FA_EPI_ADD */
+  const float* vec;    /* FA_EPI_BIAS: device [head_dim]; NULL for the other kinds */
 } fa_epilogue_op;
 
 #define FA_MAX_EPILOGUE 8

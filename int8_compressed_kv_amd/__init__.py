@@ -22,14 +22,14 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Mul", "Add", "compress_kv", "append_kv", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
+__all__ = ["Mul", "Add", "Bias", "ReLU", "compress_kv", "append_kv", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
            "decode_num_splits", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
            "F32", "BF16", "I8"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 F32, BF16, I8 = 0, 1, 2
-_EPI_MUL, _EPI_ADD = 1, 2
+_EPI_MUL, _EPI_ADD, _EPI_BIAS, _EPI_RELU = 1, 2, 3, 4
 _MAX_EPI = 8
 
 
@@ -53,8 +53,19 @@ class Add:
     value: float
 
 
+@dataclass(frozen=True, eq=False)
+class Bias:
+    """Epilogue op: out[..., c] = out[..., c] + vec[c] for a device fp32 vector of head_dim values."""
+    vec: object
+
+
+@dataclass(frozen=True)
+class ReLU:
+    """Epilogue op: out = max(out, 0) (x > 0 ? x : +0)."""
+
+
 class _EpiOp(ctypes.Structure):
-    _fields_ = [("kind", ctypes.c_int32), ("value", ctypes.c_float)]
+    _fields_ = [("kind", ctypes.c_int32), ("value", ctypes.c_float), ("vec", ctypes.c_void_p)]
 
 
 _lib = None
@@ -147,18 +158,28 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def _epilogue(ops):
+def _epilogue(ops, head_dim=None):
     ops = list(ops or [])
     if len(ops) > _MAX_EPI:
         raise ValueError(f"at most {_MAX_EPI} epilogue ops")
     arr = (_EpiOp * max(1, len(ops)))()
     for i, op in enumerate(ops):
         if isinstance(op, Mul):
-            arr[i] = _EpiOp(_EPI_MUL, float(op.value))
+            arr[i] = _EpiOp(_EPI_MUL, float(op.value), None)
         elif isinstance(op, Add):
-            arr[i] = _EpiOp(_EPI_ADD, float(op.value))
+            arr[i] = _EpiOp(_EPI_ADD, float(op.value), None)
+        elif isinstance(op, Bias):
+            torch = _torch()
+            vec = op.vec
+            if not isinstance(vec, torch.Tensor) or vec.dtype != torch.float32 or vec.dim() != 1:
+                raise ValueError("Bias needs a 1-D fp32 device tensor")
+            if head_dim is not None and vec.numel() != head_dim:
+                raise ValueError(f"Bias vector has {vec.numel()} values, head_dim is {head_dim}")
+            arr[i] = _EpiOp(_EPI_BIAS, 0.0, _dev(vec, "bias vector"))
+        elif isinstance(op, ReLU):
+            arr[i] = _EpiOp(_EPI_RELU, 0.0, None)
         else:
-            raise TypeError(f"epilogue ops must be Mul or Add, got {op!r}")
+            raise TypeError(f"epilogue ops must be Mul, Add, Bias or ReLU, got {op!r}")
     return arr, len(ops)
 
 
@@ -229,7 +250,7 @@ def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(),
     if out is None:
         out = torch.empty((bh_q, s_q, d), dtype=odt, device=q.device)
     lse = torch.empty((bh_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
-    epi, n_epi = _epilogue(epilogue)
+    epi, n_epi = _epilogue(epilogue, d)
     _check(lib().fa_forward(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dtype_code(k),
                             _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"),
                             _out_code(out.dtype), _dev(lse, "lse"), bh_q, bh_kv, s_q, s_k, d,
@@ -256,7 +277,7 @@ def merge_lse(o_parts, lse_parts, *, epilogue=(), out_dtype=None, out=None, retu
     if tuple(out.shape) != tuple(o_parts.shape[1:]):
         raise ValueError("out must have the shape of one part")
     lse = torch.empty(tuple(lse_parts.shape[1:]), dtype=torch.float32, device=o_parts.device) if return_lse else None
-    epi, n_epi = _epilogue(epilogue)
+    epi, n_epi = _epilogue(epilogue, d)
     _check(lib().fa_merge_lse(_dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts"), n_parts, rows, d,
                               _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"), epi, n_epi, _stream()))
     return (out, lse) if return_lse else out
@@ -292,7 +313,7 @@ def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epi
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     lse = torch.empty((bh_q,), dtype=torch.float32, device=q.device) if return_lse else None
-    epi, n_epi = _epilogue(epilogue)
+    epi, n_epi = _epilogue(epilogue, d)
     _check(lib().fa_decode(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dev(k_scale, "k_scale"),
                            _dev(v_scale, "v_scale"), _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"),
                            bh_q, bh_kv, s_k, d, float(scale) if scale else 0.0, int(window), int(num_splits),

@@ -50,10 +50,16 @@ int fill_epilogue(const fa_epilogue_op* epi, int32_t n_epi, fa::EpiArgs* out) {
     return fail(FA_ERR_UNSUPPORTED, "at most %d epilogue ops are supported (got %d)", FA_MAX_EPILOGUE, n_epi);
   if (n_epi > 0 && epi == nullptr) return fail(FA_ERR_INVALID, "epi is NULL but n_epi = %d", n_epi);
   for (int i = 0; i < n_epi; ++i) {
-    if (epi[i].kind != FA_EPI_MUL && epi[i].kind != FA_EPI_ADD)
-      return fail(FA_ERR_INVALID, "epilogue op %d has unknown kind %d", i, epi[i].kind);
-    out->kind[i] = epi[i].kind;
+    const int k = epi[i].kind;
+    if (k != FA_EPI_MUL && k != FA_EPI_ADD && k != FA_EPI_BIAS && k != FA_EPI_RELU)
+      return fail(FA_ERR_INVALID, "epilogue op %d has unknown kind %d", i, k);
+    if (k == FA_EPI_BIAS && (!epi[i].vec || (reinterpret_cast<uintptr_t>(epi[i].vec) & 3u)))
+      return fail(FA_ERR_INVALID, "epilogue op %d (bias) needs a 4-byte aligned device vector", i);
+    if (k != FA_EPI_BIAS && epi[i].vec)
+      return fail(FA_ERR_INVALID, "epilogue op %d: vec must be NULL unless the kind is FA_EPI_BIAS", i);
+    out->kind[i] = k;
     out->value[i] = epi[i].value;
+    out->vec[i] = epi[i].vec;
   }
   out->n = n_epi;
   return FA_OK;
@@ -70,7 +76,7 @@ constexpr int32_t kDecodeTile = 32;   // keys per decode tile
 
 extern "C" {
 
-int32_t fa_version(void) { return 10000; }
+int32_t fa_version(void) { return 10100; }
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 

@@ -485,7 +485,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   float y[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) y[e] = o[e] * inv;
-  apply_epilogue_all(y, a.epi);
+  apply_epilogue_all(y, a.epi, [&](int e) { return min(lane + 64 * e, D - 1); });   // lanes past D discard
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int d = lane + 64 * e;

@@ -114,26 +114,41 @@ __device__ __forceinline__ float add_xor16(float x) {
 // ---------------------------------------------------------------------------------------
 // Epilogue: ops applied in list order in fp32, each a separately rounded IEEE operation
 // (no contraction into FMA), so the fused result equals the same ops applied on the host.
+// Mul and Add take a scalar, Bias adds a per-channel vector (channel = head-dim index of the
+// output element), ReLU maps x to x > 0 ? x : +0.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ float apply_epilogue(float x, const EpiArgs& e) {
-  for (int i = 0; i < e.n; ++i) {
-    const float c = e.value[i];
-    x = (e.kind[i] == kEpiMul) ? __fmul_rn(x, c) : __fadd_rn(x, c);
-  }
+__device__ __forceinline__ float epilogue_op(float x, int kind, float c, const float* vec, int channel) {
+  if (kind == kEpiMul) return __fmul_rn(x, c);
+  if (kind == kEpiAdd) return __fadd_rn(x, c);
+  if (kind == kEpiBias) return __fadd_rn(x, vec[channel]);
+  return x > 0.f ? x : 0.f;
+}
+
+__device__ __forceinline__ float apply_epilogue(float x, const EpiArgs& e, int channel) {
+  for (int i = 0; i < e.n; ++i) x = epilogue_op(x, e.kind[i], e.value[i], e.vec[i], channel);
   return x;
 }
 
-// The same ops over an array, op-major: one uniform branch per op.
-template <int N>
-__device__ __forceinline__ void apply_epilogue_all(float (&x)[N], const EpiArgs& e) {
+// The same ops over an array, op-major (one uniform branch per op); channel(j) is the head-dim
+// index of x[j].
+template <int N, class Channel>
+__device__ __forceinline__ void apply_epilogue_all(float (&x)[N], const EpiArgs& e, Channel channel) {
   for (int i = 0; i < e.n; ++i) {
+    const int kind = e.kind[i];
     const float cv = e.value[i];
-    if (e.kind[i] == kEpiMul) {
+    if (kind == kEpiMul) {
 #pragma unroll
       for (int j = 0; j < N; ++j) x[j] = __fmul_rn(x[j], cv);
-    } else {
+    } else if (kind == kEpiAdd) {
 #pragma unroll
       for (int j = 0; j < N; ++j) x[j] = __fadd_rn(x[j], cv);
+    } else if (kind == kEpiBias) {
+      const float* vec = e.vec[i];
+#pragma unroll
+      for (int j = 0; j < N; ++j) x[j] = __fadd_rn(x[j], vec[channel(j)]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < N; ++j) x[j] = x[j] > 0.f ? x[j] : 0.f;
     }
   }
 }

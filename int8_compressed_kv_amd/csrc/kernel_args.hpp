@@ -10,11 +10,14 @@ namespace fa {
 constexpr int kMaxEpilogue = 8;
 constexpr int kEpiMul = 1;
 constexpr int kEpiAdd = 2;
+constexpr int kEpiBias = 3;   // + vec[channel]
+constexpr int kEpiRelu = 4;   // max(x, +0)
 
 struct EpiArgs {
   int32_t n;
   int32_t kind[kMaxEpilogue];
   float value[kMaxEpilogue];
+  const float* vec[kMaxEpilogue];   // per-channel vector of a bias op, else null
 };
 
 enum DType : int32_t { kF32 = 0, kBF16 = 1, kI8 = 2 };

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   float y[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[e] = acc[e] * inv;
-  apply_epilogue_all(y, a.epi);
+  apply_epilogue_all(y, a.epi, [&](int e) { return 4 * sl + e; });
   if (a.out_bf16) {
     const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + 4 * sl) = w;

@@ -433,7 +433,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[16 * db + i] = O[db][i] * inv;
-    apply_epilogue_all(y, a.epi);
+    // element 16 db + i sits at head-dim 32 db + 8 (i / 4) + 4 h + i % 4
+    apply_epilogue_all(y, a.epi, [&](int j) { return 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * h + j % 4; });
     const int64_t row = (int64_t)head * a.s_q + qi;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
         const int d0 = 32 * b + 8 * g + 4 * h;
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = apply_epilogue(O[b][4 * g + e] * inv, a.epi);
+        for (int e = 0; e < 4; ++e) y[e] = apply_epilogue(O[b][4 * g + e] * inv, a.epi, d0 + e);
         if (a.out_bf16) {
           u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
           *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + d0) = w;

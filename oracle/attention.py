@@ -72,9 +72,13 @@ def visible_mask(s_q: int, s_k: int, causal: bool, window: int = 0) -> np.ndarra
 
 
 def apply_epilogue(x: np.ndarray, ops) -> np.ndarray:
-    """Apply the post-ops in list order, in fp64.  ops: iterable of ("mul"|"add", value).
+    """Apply the post-ops in list order, in fp64.  ops: iterable of (kind, value) with kind
+    "mul" / "add" (scalar value), "bias" (value: a vector over the last axis, the head dim) or
+    "relu" (value ignored; x > 0 ? x : 0).
 
-    fkl PR, Summary: epilogue=[fkl.Mul(2.0), fkl.Add(0.5)] scales then shifts the output.
+    fkl PR, Summary: epilogue=[fkl.Mul(2.0), fkl.Add(0.5)] scales then shifts the output, and
+    any compute op may be chained; kernbench2 commit page (the tl.composite epilogue list):
+    bias, relu and scale ops applied in order to an output tile.
     """
     y = np.array(x, dtype=np.float64, copy=True)
     for kind, val in ops:
@@ -82,6 +86,13 @@ def apply_epilogue(x: np.ndarray, ops) -> np.ndarray:
             y = y * float(val)
         elif kind == "add":
             y = y + float(val)
+        elif kind == "bias":
+            b = np.asarray(val, dtype=np.float64)
+            if b.shape != y.shape[-1:]:
+                raise ValueError("a bias vector has one value per head-dim channel")
+            y = y + b
+        elif kind == "relu":
+            y = np.where(y > 0, y, 0.0)
         else:
             raise ValueError(f"unknown epilogue op {kind!r}")
     return y

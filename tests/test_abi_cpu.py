@@ -177,3 +177,26 @@ def test_merge_rejects_invalid_arguments_on_host(L, kw, code):
 
 def test_merge_zero_rows_is_a_noop(L):
     assert _mrg(L, rows=0, o=0, l=0, out=0) == 0
+
+
+def test_bias_and_relu_ops_are_validated_on_host(L):
+    E = fa._EpiOp
+    ok = (E * 2)(E(4, 0.0, None), E(3, 0.0, 1 << 20))
+    assert _fwd(L, epi=ok, n_epi=2, q=0) == -1 and "null q" in fa.last_error()   # ops accepted; fails later
+    no_vec = (E * 1)(E(3, 0.0, None))
+    assert _fwd(L, epi=no_vec, n_epi=1) == -1 and "bias" in fa.last_error()
+    odd_vec = (E * 1)(E(3, 0.0, (1 << 20) + 2))
+    assert _fwd(L, epi=odd_vec, n_epi=1) == -1
+    stray_vec = (E * 1)(E(4, 0.0, 1 << 20))
+    assert _fwd(L, epi=stray_vec, n_epi=1) == -1 and "NULL" in fa.last_error()
+    assert ctypes.sizeof(E) == 16   # int32 kind, float value, pointer vec
+
+
+def test_python_epilogue_ops_check_the_bias_vector():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        fa._epilogue([fa.Bias(torch.zeros(64, dtype=torch.float64))], 64)
+    with pytest.raises(ValueError):
+        fa._epilogue([fa.Bias(torch.zeros(32))], 64)
+    arr, n = fa._epilogue([fa.ReLU(), fa.Mul(2.0)], 64)
+    assert n == 2 and arr[0].kind == 4 and arr[1].kind == 1

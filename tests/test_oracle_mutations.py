@@ -172,3 +172,25 @@ def test_merge_with_max_instead_of_logsumexp_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "merge_lse", max_lse)
     with pytest.raises(AssertionError):
         pin()
+
+
+def test_relu_as_abs_or_bias_reversed_is_caught(monkeypatch):
+    from test_oracle_pins import test_bias_relu_chain_matches_brute_force as pin
+    pin()
+    orig = oatt.apply_epilogue
+
+    monkeypatch.setattr(oatt, "apply_epilogue", lambda x, ops: _abs_variant(orig, x, ops))
+    with pytest.raises(AssertionError):
+        pin()
+    monkeypatch.setattr(oatt, "apply_epilogue",
+                        lambda x, ops: orig(x, [(k, v[::-1]) if k == "bias" else (k, v) for k, v in ops]))
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def _abs_variant(orig, x, ops):
+    """The epilogue with relu planted as abs."""
+    y = np.array(x, dtype=np.float64)
+    for k, v in ops:
+        y = np.abs(y) if k == "relu" else orig(y, [(k, v)])
+    return y

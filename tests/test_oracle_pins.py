@@ -49,7 +49,14 @@ def brute_attention(q, k, v, causal, window, scale, group, ops=(), ks=None, vs=N
             z = math.fsum(w.values())
             row = [math.fsum(w[j] * vv[j][c] for j in keys) / z for c in range(d)]
             for kind, val in ops:
-                row = [x * val if kind == "mul" else x + val for x in row]
+                if kind == "mul":
+                    row = [x * val for x in row]
+                elif kind == "add":
+                    row = [x + val for x in row]
+                elif kind == "bias":
+                    row = [x + float(val[c]) for c, x in enumerate(row)]
+                else:
+                    row = [x if x > 0 else 0.0 for x in row]
             out[h][i] = row
             lse[h][i] = m + math.log(z)
     return np.array(out), np.array(lse)
@@ -272,7 +279,15 @@ def test_epilogue_order_and_values():
     np.testing.assert_array_equal(oracle.apply_epilogue(x, [("add", 0.5), ("mul", 2.0)]), 2 * x + 1.0)
     np.testing.assert_array_equal(oracle.apply_epilogue(x, []), x)
     with pytest.raises(ValueError):
-        oracle.apply_epilogue(x, [("relu", 0.0)])
+        oracle.apply_epilogue(x, [("gelu", 0.0)])
+    # per-channel bias and relu, worked by hand
+    b = [10.0, -1.0, 0.5]
+    np.testing.assert_array_equal(oracle.apply_epilogue(x, [("bias", b)]), [[9.0, -0.75, 3.5]])
+    np.testing.assert_array_equal(oracle.apply_epilogue(x, [("relu", None)]), [[0.0, 0.25, 3.0]])
+    np.testing.assert_array_equal(oracle.apply_epilogue(x, [("bias", b), ("relu", None), ("mul", -2.0)]),
+                                  [[-18.0, 0.0, -7.0]])
+    with pytest.raises(ValueError):
+        oracle.apply_epilogue(x, [("bias", [1.0, 2.0])])
 
 
 def test_window_without_causal_rejected():
@@ -451,3 +466,15 @@ def test_merge_special_cases():
     assert np.allclose(out[2], o[0, 2], atol=1e-15) and l[2] == 2.0
     assert np.allclose(out[3], o.mean(axis=0)[3], atol=1e-15) and np.isclose(l[3], 1.0 + np.log(3))
     assert np.allclose(out[4], o[1, 4], atol=1e-15) and l[4] == 3.0   # parts 0 and 2 empty
+
+
+def test_bias_relu_chain_matches_brute_force():
+    """A chain with a per-channel bias and a relu, through the whole attention, against the
+    pure-Python loops (which apply the ops element by element)."""
+    q, k, v = rng_normal(39, (3, 4, 8), (1, 6, 8), (1, 6, 8))
+    bias = rng_normal(40, (8,))[0]
+    ops = [("mul", 3.0), ("bias", bias.tolist()), ("relu", None), ("add", -0.25)]
+    o_ref, _ = brute_attention(q.tolist(), k.tolist(), v.tolist(), True, 0, 1 / math.sqrt(8), 3, ops)
+    o, _ = oracle.attention(q, k, v, causal=True, epilogue=ops)
+    assert np.abs(o - o_ref).max() < 1e-13
+    assert (o_ref == -0.25).any() and (o_ref > -0.25).any()     # the relu both clipped and passed
