@@ -12,6 +12,8 @@ Modules
                 the merge of results over disjoint key sets by log-sum-exp.
   quantize   -- the per-token absmax/127 int8 quantizer (numpy fp32), the
                 closed-form compression ratio and the decode-time cache write.
+  turboquant -- the 2-4-bit TurboQuant codec: randomized Hadamard rotation, L2
+                normalisation, Lloyd-Max codebooks for Beta(d/2, d/2), packing.
 
 Every function is pinned by tests in tests/test_oracle_pins.py (brute force,
 a library cross-check, invariants and closed forms).  No function here is
@@ -19,3 +21,5 @@ a library cross-check, invariants and closed forms).  No function here is
 """
 from .attention import attention, apply_epilogue, dequantize, visible_mask, decode, merge_lse  # noqa: F401
 from .quantize import quantize_per_token, compression_ratio, append_kv  # noqa: F401
+from .turboquant import (hadamard, beta_codebook, tq_encode, tq_decode, tq_pack, tq_unpack,  # noqa: F401
+                         tq_compression_ratio)

@@ -26,7 +26,7 @@ import dataclasses
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "draw_qkv", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "round_bf16", "rng_normal"]
+           "bf16_bits_to_f32", "round_bf16", "rng_normal", "random_signs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -104,3 +104,10 @@ def draw_qkv(w: Workload, bh_kv: int | None = None, s_q: int | None = None,
         k = round_bf16(k)
         v = round_bf16(v)
     return q, k, v
+
+
+def random_signs(seed: int, n: int) -> np.ndarray:
+    """n independent fair +-1 signs (int8) from PCG64(seed): the random diagonal the TurboQuant
+    rotation draws, passed to both the oracle and the library as an input."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return np.where(g.random(n) < 0.5, -1, 1).astype(np.int8)
