@@ -10,6 +10,7 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   comp   per-token compression of the c4 K and V caches (fp32 -> int8 + fp32 scales)
   append decode-time cache write of the c4 shape: one new fp32 K and V token per KV head (128),
          quantized into the 32768-row int8 cache at device-held positions (latency-bound)
+  tq     TurboQuant 4-bit encode of the c4 K cache (fp32 in) and decode of it back to bf16
   merge  log-sum-exp merge of 8 key-chunk results for one 4096-row query chunk of the c5 shape
          (64 heads x 4096 rows, d 128, fp32 parts, bf16 output): the exchange of a ring prefill
   copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
@@ -57,6 +58,7 @@ LEG_SOURCES = {
     "comp": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
     "append": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
     "merge": ("merge.hip", "device_common.hpp", "kernel_args.hpp"),
+    "tq": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
@@ -120,7 +122,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp,append,merge")
+    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp,append,merge,tq")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
     args = ap.parse_args()
@@ -193,7 +195,7 @@ def main():
         del qd, kc, ks, vc, vs, out, q, k, v
 
     # ------------------------------------------------------------------ compress + decode c4
-    if legs & {"c4", "comp", "append"}:
+    if legs & {"c4", "comp", "append", "tq"}:
         w = WORKLOADS["c4"]
         log(f"[bench] generating {w.name}")
         q, k, v = draw_qkv(w)
@@ -215,6 +217,32 @@ def main():
                            "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                            "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] comp: {avg:.3f} ms  {res['comp']['gbs']:.0f} GB/s")
+        if "tq" in legs:
+            from synth_inputs import random_signs
+            bits = 4
+            cb = fa.tq_codebook(w.d, bits)
+            signs = torch.from_numpy(random_signs(64, w.d)).cuda()
+            codes = torch.empty((w.bh_kv, w.s_k, w.d * bits // 8), dtype=torch.uint8, device="cuda")
+            norms = torch.empty((w.bh_kv, w.s_k), dtype=torch.float32, device="cuda")
+            fn = lambda: fa.tq_encode(kf, signs, bits, cb, codes, norms)   # noqa: E731
+            log("[bench] timing TurboQuant encode (c4 K cache, 4 bits)")
+            ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = n_tok * (w.d * 4 + w.d * bits // 8 + 4)
+            res["tq"] = {"workload": "tq4_encode_c4_k_cache_128x32768x128_f32", "ms": avg, "ms_min": float(np.min(ms)),
+                         "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
+                         "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] tq encode: {avg:.3f} ms  {res['tq']['gbs']:.0f} GB/s")
+            kb16 = torch.empty(kf.shape, dtype=torch.bfloat16, device="cuda")
+            fn = lambda: fa.tq_decode(codes, norms, signs, bits, cb, out=kb16)   # noqa: E731
+            ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = n_tok * (w.d * bits // 8 + 4 + w.d * 2)
+            res["tq_dec"] = {"workload": "tq4_decode_c4_k_cache_128x32768x128_to_bf16", "ms": avg,
+                             "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "bytes_per_launch": nbytes,
+                             "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] tq decode: {avg:.3f} ms  {res['tq_dec']['gbs']:.0f} GB/s")
+            del codes, norms, kb16, signs
         fa.compress_kv(kf, kc, ks)
         fa.compress_kv(vf, vc, vs)
         if "append" in legs:

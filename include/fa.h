@@ -19,6 +19,11 @@
  *                      normalised outputs and log-sum-exps, the state a split or ring
  *                      prefill exchanges (kernbench2 ADR-0060 commit: partial (m, l, O)
  *                      states reduced into one).
+ *   fa_tq_codebook, fa_tq_encode, fa_tq_decode
+ *                   -- the TurboQuant 2/4-bit KV codec: randomized Hadamard rotation,
+ *                      L2 normalisation, Lloyd-Max codebook of the Beta(d/2, d/2)
+ *                      coordinate law, bit-packing (Foundry attention/ README, section
+ *                      "TurboQuant KV Cache Compression").
  *   fa_decode       -- one query row per head against an int8 cache, split over the
  *                      keys with a log-sum-exp merge of the partial (m, l, O) states
  *                      (fkl PR, Verification: the decode check; kernbench2 ADR-0060
@@ -155,6 +160,38 @@ int fa_forward(const void* q, int32_t q_dtype,
 int fa_merge_lse(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows, int32_t head_dim,
                  void* out, int32_t out_dtype, float* lse_out, const fa_epilogue_op* epi, int32_t n_epi,
                  void* stream);
+
+/*
+ * fa_tq_codebook -- the 2^bits Lloyd-Max centroids (ascending, written to the host array
+ * `centroids`) of u = 2B - 1 with B ~ Beta(head_dim/2, head_dim/2), the coordinate law the
+ * TurboQuant page quantizes against (Foundry attention/ README, TurboQuant section).  Computed
+ * on the host (Lloyd-Max iterations, Gauss-Legendre quadrature), about 0.1 s; callers keep it.
+ * head_dim in {32, 64, 128, 256}, bits in {2, 4}.
+ */
+int fa_tq_codebook(int32_t head_dim, int32_t bits, float* centroids);
+
+/*
+ * fa_tq_encode -- TurboQuant codes of n_tokens vectors.
+ *   x          device [n_tokens, head_dim], FA_F32 or FA_BF16.
+ *   signs      device int8 [head_dim], each +1 or -1: the random diagonal of the rotation.
+ *   codebook   host fp32 [2^bits], strictly increasing (fa_tq_codebook's output).
+ *   codes_out  device uint8 [n_tokens, head_dim * bits / 8]; channel i's code at bit
+ *              (i bits) mod 8 of byte (i bits) / 8.
+ *   norms_out  device fp32 [n_tokens]: ||x||_2.
+ * y = H (signs * x) (Sylvester Hadamard), u = y / ||y||, code_i = the number of midpoints
+ * between consecutive centroids that are <= u_i.  Decisions are taken in fp32.
+ * n_tokens == 0 is a no-op.
+ */
+int fa_tq_encode(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_dim, int32_t bits,
+                 const int8_t* signs, const float* codebook, uint8_t* codes_out, float* norms_out,
+                 void* stream);
+
+/*
+ * fa_tq_decode -- x_hat = signs * H (norm * codebook[code]) / sqrt(head_dim), written as out_dtype
+ * (FA_F32 or FA_BF16) to device out [n_tokens, head_dim].  Arguments as for fa_tq_encode.
+ */
+int fa_tq_decode(const uint8_t* codes, const float* norms, int64_t n_tokens, int32_t head_dim, int32_t bits,
+                 const int8_t* signs, const float* codebook, void* out, int32_t out_dtype, void* stream);
 
 /*
  * fa_decode_num_splits -- the split count fa_decode uses when num_splits == 0.

@@ -13,6 +13,9 @@ present, the calls raise.
     append_kv(k1, v1, pos, kc, vc, ks, vs)               # quantize new tokens into the cache
     out = decode(q1, kc, vc, ks, vs)                     # split-KV decode step
     out = merge_lse(o_parts, lse_parts)                  # attention over a union of key chunks
+    cb = tq_codebook(128, 4)                             # TurboQuant: Lloyd-Max codebook (host)
+    codes, norms = tq_encode(k, signs, 4, cb)            # 4-bit codes + fp32 norm per token
+    k_hat = tq_decode(codes, norms, signs, 4, cb)        # back to fp32 / bf16
 
 Layout (batch*heads, seq, head_dim), head_dim a multiple of 32 up to 256.
 """
@@ -22,7 +25,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Mul", "Add", "Bias", "ReLU", "compress_kv", "append_kv", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
+__all__ = ["Mul", "Add", "Bias", "ReLU", "compress_kv", "append_kv", "tq_codebook", "tq_encode", "tq_decode", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
            "decode_num_splits", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
            "F32", "BF16", "I8"]
 
@@ -87,6 +90,12 @@ def lib() -> ctypes.CDLL:
     L.fa_forward.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                              i32, i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(_EpiOp), i32, vp]
     L.fa_forward.restype = ctypes.c_int
+    L.fa_tq_codebook.argtypes = [i32, i32, vp]
+    L.fa_tq_codebook.restype = ctypes.c_int
+    L.fa_tq_encode.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp, vp]
+    L.fa_tq_encode.restype = ctypes.c_int
+    L.fa_tq_decode.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, i32, vp]
+    L.fa_tq_decode.restype = ctypes.c_int
     L.fa_merge_lse.argtypes = [vp, vp, i32, i64, i32, vp, i32, vp, ctypes.POINTER(_EpiOp), i32, vp]
     L.fa_merge_lse.restype = ctypes.c_int
     L.fa_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -257,6 +266,54 @@ def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(),
                             float(scale) if scale else 0.0, int(bool(causal)), int(window), epi, n_epi,
                             _stream()))
     return (out, lse) if return_lse else out
+
+
+def tq_codebook(head_dim: int, bits: int):
+    """The library's TurboQuant Lloyd-Max centroids (2^bits, ascending) as a host float32 array."""
+    import numpy as np
+    out = np.zeros(1 << bits, np.float32)
+    _check(lib().fa_tq_codebook(int(head_dim), int(bits), ctypes.c_void_p(out.ctypes.data)))
+    return out
+
+
+def _host_f32(cb):
+    import numpy as np
+    cb = np.ascontiguousarray(np.asarray(cb, dtype=np.float32))
+    return cb, ctypes.c_void_p(cb.ctypes.data)
+
+
+def tq_encode(x, signs, bits, codebook, codes=None, norms=None):
+    """TurboQuant codes (..., head_dim * bits / 8) uint8 and fp32 norms (...) of fp32/bf16 rows x
+    (..., head_dim); signs: int8 +-1 device tensor (head_dim,); codebook: host (2^bits,) centroids."""
+    torch = _torch()
+    d = x.shape[-1]
+    n = x.numel() // d if d else 0
+    if signs.dtype != torch.int8 or tuple(signs.shape) != (d,):
+        raise ValueError("signs must be an int8 tensor of shape (head_dim,)")
+    if codes is None:
+        codes = torch.empty(tuple(x.shape[:-1]) + (d * bits // 8,), dtype=torch.uint8, device=x.device)
+    if norms is None:
+        norms = torch.empty(tuple(x.shape[:-1]), dtype=torch.float32, device=x.device)
+    cb, cbp = _host_f32(codebook)
+    _check(lib().fa_tq_encode(_dev(x, "x"), _dtype_code(x), n, d, int(bits), _dev(signs, "signs"), cbp,
+                              _dev(codes, "codes"), _dev(norms, "norms"), _stream()))
+    return codes, norms
+
+
+def tq_decode(codes, norms, signs, bits, codebook, out_dtype=None, out=None):
+    """Rows (..., head_dim) decoded from TurboQuant codes and norms (fp32 by default)."""
+    torch = _torch()
+    d = signs.shape[0]
+    if codes.dtype != torch.uint8 or codes.shape[-1] != d * bits // 8:
+        raise ValueError("codes must be uint8 (..., head_dim * bits / 8)")
+    n = norms.numel()
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(tuple(codes.shape[:-1]) + (d,), dtype=odt, device=codes.device)
+    cb, cbp = _host_f32(codebook)
+    _check(lib().fa_tq_decode(_dev(codes, "codes"), _dev(norms, "norms"), n, d, int(bits), _dev(signs, "signs"),
+                              cbp, _dev(out, "out"), _out_code(out.dtype), _stream()))
+    return out
 
 
 def merge_lse(o_parts, lse_parts, *, epilogue=(), out_dtype=None, out=None, return_lse=False):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 
-HIP_SOURCES = ["compress.hip", "prefill_f32.hip", "prefill_bf16.hip", "prefill_i8kv.hip", "decode.hip", "merge.hip"]
+HIP_SOURCES = ["compress.hip", "prefill_f32.hip", "prefill_bf16.hip", "prefill_i8kv.hip", "decode.hip", "merge.hip", "tq.hip"]
 CPP_SOURCES = ["api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", CSRC, "-I", INCLUDE,

@@ -233,6 +233,82 @@ int fa_merge_lse(const float* o_parts, const float* lse_parts, int32_t n_parts, 
   return FA_OK;
 }
 
+namespace {
+int check_tq(int32_t head_dim, int32_t bits) {
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(FA_ERR_UNSUPPORTED, "TurboQuant needs a power-of-two head_dim in [32, 256] (got %d)", head_dim);
+  if (bits != 2 && bits != 4) return fail(FA_ERR_UNSUPPORTED, "TurboQuant bits must be 2 or 4 (got %d)", bits);
+  return FA_OK;
+}
+int check_codebook(const float* cb, int32_t bits) {
+  if (!cb) return fail(FA_ERR_INVALID, "null codebook");
+  for (int k = 1; k < (1 << bits); ++k)
+    if (!(cb[k] > cb[k - 1])) return fail(FA_ERR_INVALID, "codebook must be strictly increasing");
+  return FA_OK;
+}
+}  // namespace
+
+int fa_tq_codebook(int32_t head_dim, int32_t bits, float* centroids) {
+  g_last_error.clear();
+  if (int r = check_tq(head_dim, bits)) return r;
+  if (!centroids) return fail(FA_ERR_INVALID, "null centroids");
+  fa::tq_codebook(head_dim, bits, centroids);
+  return FA_OK;
+}
+
+int fa_tq_encode(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_dim, int32_t bits,
+                 const int8_t* signs, const float* codebook, uint8_t* codes_out, float* norms_out, void* stream) {
+  g_last_error.clear();
+  if (int r = check_tq(head_dim, bits)) return r;
+  if (x_dtype != FA_F32 && x_dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "tq_encode input must be FA_F32 or FA_BF16 (got %d)", x_dtype);
+  if (n_tokens < 0) return fail(FA_ERR_INVALID, "n_tokens must be >= 0");
+  if (int r = check_codebook(codebook, bits)) return r;
+  if (n_tokens == 0) return FA_OK;
+  if (!x || !signs || !codes_out || !norms_out) return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(x) || !aligned16(codes_out) || (reinterpret_cast<uintptr_t>(norms_out) & 3u))
+    return fail(FA_ERR_INVALID, "x and codes must be 16-byte aligned, norms 4-byte aligned");
+  fa::TqArgs a{};
+  a.x = x;
+  a.signs = signs;
+  a.codes = codes_out;
+  a.norms = norms_out;
+  a.n = n_tokens;
+  a.inv_sqrt_d = 1.0f / std::sqrt((float)head_dim);
+  for (int k = 0; k + 1 < (1 << bits); ++k) a.thr[k] = 0.5f * (codebook[k] + codebook[k + 1]);
+  const char* name = "";
+  hipError_t e = fa::launch_tq_encode(a, head_dim, bits, x_dtype, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "tq_encode launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
+int fa_tq_decode(const uint8_t* codes, const float* norms, int64_t n_tokens, int32_t head_dim, int32_t bits,
+                 const int8_t* signs, const float* codebook, void* out, int32_t out_dtype, void* stream) {
+  g_last_error.clear();
+  if (int r = check_tq(head_dim, bits)) return r;
+  if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "out dtype must be FA_F32 or FA_BF16");
+  if (n_tokens < 0) return fail(FA_ERR_INVALID, "n_tokens must be >= 0");
+  if (int r = check_codebook(codebook, bits)) return r;
+  if (n_tokens == 0) return FA_OK;
+  if (!codes || !norms || !signs || !out) return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(norms) & 3u))
+    return fail(FA_ERR_INVALID, "codes and out must be 16-byte aligned, norms 4-byte aligned");
+  fa::TqArgs a{};
+  a.signs = signs;
+  a.codes = const_cast<uint8_t*>(codes);
+  a.norms = const_cast<float*>(norms);
+  a.out = out;
+  a.n = n_tokens;
+  a.inv_sqrt_d = 1.0f / std::sqrt((float)head_dim);
+  for (int k = 0; k < (1 << bits); ++k) a.cb[k] = codebook[k];
+  const char* name = "";
+  hipError_t e = fa::launch_tq_decode(a, head_dim, bits, out_dtype == FA_BF16, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "tq_decode launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
+
 int32_t fa_decode_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim) {
   (void)head_dim;
   if (bh_kv <= 0 || bh_q <= 0 || s_k <= 0) return 1;

@@ -80,6 +80,18 @@ struct MergeArgs {
   EpiArgs epi;
 };
 
+struct TqArgs {
+  const void* x;          // encode input [n, d] fp32 or bf16
+  const int8_t* signs;    // [d], +-1
+  uint8_t* codes;         // [n, d bits / 8] packed codes (written by encode, read by decode)
+  float* norms;           // [n]
+  void* out;              // decode output [n, d]
+  int64_t n;
+  float inv_sqrt_d;
+  float thr[15];          // encode: the 2^bits - 1 thresholds, ascending
+  float cb[16];           // decode: the 2^bits centroids, ascending
+};
+
 // Launchers return hipSuccess or the launch error; *name receives the instantiation name.
 hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d,
                            int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);
@@ -90,5 +102,10 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, hipStream_t stre
 hipError_t launch_prefill_i8kv(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_merge(const MergeArgs& a, int32_t d, hipStream_t stream, const char** name);
+hipError_t launch_tq_encode(const TqArgs& a, int32_t d, int32_t bits, int32_t x_dtype, hipStream_t stream,
+                            const char** name);
+hipError_t launch_tq_decode(const TqArgs& a, int32_t d, int32_t bits, bool bf16_out, hipStream_t stream,
+                            const char** name);
+int tq_codebook(int32_t d, int32_t bits, float* centroids);   // host
 
 }  // namespace fa

@@ -69,6 +69,7 @@ def beta_codebook(d: int, bits: int, iters: int = 20000, tol: float = 1e-15):
         c = c_new
         if done:
             break
+    c = (c - c[::-1]) / 2          # the law is symmetric, so is its codebook: remove iteration round-off
     return c, (c[:-1] + c[1:]) / 2
 
 

@@ -200,3 +200,33 @@ def test_python_epilogue_ops_check_the_bias_vector():
         fa._epilogue([fa.Bias(torch.zeros(32))], 64)
     arr, n = fa._epilogue([fa.ReLU(), fa.Mul(2.0)], 64)
     assert n == 2 and arr[0].kind == 4 and arr[1].kind == 1
+
+
+def test_tq_codebook_on_host_matches_the_oracle_in_fp32(L):
+    import numpy as np
+    import oracle
+    for d in (32, 64, 128, 256):
+        for bits in (2, 4):
+            cb = fa.tq_codebook(d, bits)
+            ref, _ = oracle.beta_codebook(d, bits)
+            assert np.abs(cb.astype(np.float64) - ref).max() < 1e-7 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("d,bits,code", [(96, 4, -2), (64, 3, -2), (512, 2, -2)])
+def test_tq_rejects_unsupported_shapes(L, d, bits, code):
+    import numpy as np
+    out = np.zeros(16, np.float32)
+    assert L.fa_tq_codebook(d, bits, ctypes.c_void_p(out.ctypes.data)) == code
+    vp = ctypes.c_void_p
+    assert L.fa_tq_encode(vp(1 << 20), 0, 4, d, bits, vp(1 << 20), vp(out.ctypes.data), vp(1 << 20), vp(1 << 20), None) == code
+
+
+def test_tq_rejects_bad_codebook_and_pointers(L):
+    import numpy as np
+    vp = ctypes.c_void_p
+    bad = np.array([0.0, 0.0, 1.0, 2.0], np.float32)
+    good = fa.tq_codebook(64, 2)
+    assert L.fa_tq_encode(vp(1 << 20), 0, 4, 64, 2, vp(1 << 20), vp(bad.ctypes.data), vp(1 << 20), vp(1 << 20), None) == -1
+    assert L.fa_tq_encode(vp(0), 0, 4, 64, 2, vp(1 << 20), vp(good.ctypes.data), vp(1 << 20), vp(1 << 20), None) == -1
+    assert L.fa_tq_encode(vp(0), 0, 0, 64, 2, vp(0), vp(good.ctypes.data), vp(0), vp(0), None) == 0
+    assert L.fa_tq_decode(vp(1 << 20), vp(1 << 20), 4, 64, 2, vp(1 << 20), vp(good.ctypes.data), vp(1 << 20), 2, None) == -2
