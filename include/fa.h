@@ -174,7 +174,8 @@ int fa_tq_codebook(int32_t head_dim, int32_t bits, float* centroids);
  * fa_tq_encode -- TurboQuant codes of n_tokens vectors.
  *   x          device [n_tokens, head_dim], FA_F32 or FA_BF16.
  *   signs      device int8 [head_dim], each +1 or -1: the random diagonal of the rotation.
- *   codebook   host fp32 [2^bits], strictly increasing (fa_tq_codebook's output).
+ *   codebook   host fp32 [2^bits], strictly increasing and antisymmetric (c[k] == -c[2^bits-1-k],
+ *              as the codebook of a symmetric law is; fa_tq_codebook's output), else FA_ERR_INVALID.
  *   codes_out  device uint8 [n_tokens, head_dim * bits / 8]; channel i's code at bit
  *              (i bits) mod 8 of byte (i bits) / 8.
  *   norms_out  device fp32 [n_tokens]: ||x||_2.
@@ -188,7 +189,8 @@ int fa_tq_encode(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_
 
 /*
  * fa_tq_decode -- x_hat = signs * H (norm * codebook[code]) / sqrt(head_dim), written as out_dtype
- * (FA_F32 or FA_BF16) to device out [n_tokens, head_dim].  Arguments as for fa_tq_encode.
+ * (FA_F32 or FA_BF16) to device out [n_tokens, head_dim].  Arguments as for fa_tq_encode, except
+ * that any strictly increasing codebook is accepted.
  */
 int fa_tq_decode(const uint8_t* codes, const float* norms, int64_t n_tokens, int32_t head_dim, int32_t bits,
                  const int8_t* signs, const float* codebook, void* out, int32_t out_dtype, void* stream);

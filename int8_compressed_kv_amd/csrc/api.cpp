@@ -264,6 +264,9 @@ int fa_tq_encode(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_
     return fail(FA_ERR_UNSUPPORTED, "tq_encode input must be FA_F32 or FA_BF16 (got %d)", x_dtype);
   if (n_tokens < 0) return fail(FA_ERR_INVALID, "n_tokens must be >= 0");
   if (int r = check_codebook(codebook, bits)) return r;
+  for (int k = 0; k < (1 << bits); ++k)
+    if (codebook[k] != -codebook[(1 << bits) - 1 - k])
+      return fail(FA_ERR_INVALID, "tq_encode codebook must be antisymmetric (c[k] == -c[2^bits - 1 - k])");
   if (n_tokens == 0) return FA_OK;
   if (!x || !signs || !codes_out || !norms_out) return fail(FA_ERR_INVALID, "null pointer argument");
   if (!aligned16(x) || !aligned16(codes_out) || (reinterpret_cast<uintptr_t>(norms_out) & 3u))

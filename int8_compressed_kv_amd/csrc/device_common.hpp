@@ -111,6 +111,17 @@ __device__ __forceinline__ float add_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One IEEE fp32 multiply or add rounded on its own: kept out of the FMA contraction that the
+// compiler otherwise applies across statements (a product feeding a sum).
+__device__ __forceinline__ float mul_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
+__device__ __forceinline__ float add_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x + y;
+}
+
 // ---------------------------------------------------------------------------------------
 // Epilogue: ops applied in list order in fp32, each a separately rounded IEEE operation
 // (no contraction into FMA), so the fused result equals the same ops applied on the host.
@@ -118,9 +129,9 @@ __device__ __forceinline__ float add_xor16(float x) {
 // output element), ReLU maps x to x > 0 ? x : +0.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ float epilogue_op(float x, int kind, float c, const float* vec, int channel) {
-  if (kind == kEpiMul) return __fmul_rn(x, c);
-  if (kind == kEpiAdd) return __fadd_rn(x, c);
-  if (kind == kEpiBias) return __fadd_rn(x, vec[channel]);
+  if (kind == kEpiMul) return mul_rn(x, c);
+  if (kind == kEpiAdd) return add_rn(x, c);
+  if (kind == kEpiBias) return add_rn(x, vec[channel]);
   return x > 0.f ? x : 0.f;
 }
 
@@ -138,14 +149,14 @@ __device__ __forceinline__ void apply_epilogue_all(float (&x)[N], const EpiArgs&
     const float cv = e.value[i];
     if (kind == kEpiMul) {
 #pragma unroll
-      for (int j = 0; j < N; ++j) x[j] = __fmul_rn(x[j], cv);
+      for (int j = 0; j < N; ++j) x[j] = mul_rn(x[j], cv);
     } else if (kind == kEpiAdd) {
 #pragma unroll
-      for (int j = 0; j < N; ++j) x[j] = __fadd_rn(x[j], cv);
+      for (int j = 0; j < N; ++j) x[j] = add_rn(x[j], cv);
     } else if (kind == kEpiBias) {
       const float* vec = e.vec[i];
 #pragma unroll
-      for (int j = 0; j < N; ++j) x[j] = __fadd_rn(x[j], vec[channel(j)]);
+      for (int j = 0; j < N; ++j) x[j] = add_rn(x[j], vec[channel(j)]);
     } else {
 #pragma unroll
       for (int j = 0; j < N; ++j) x[j] = x[j] > 0.f ? x[j] : 0.f;

@@ -9,8 +9,9 @@
 //   packed little-endian, channel i at bit (i b) mod 8 of byte (i b) / 8; n stored as fp32.
 // Decode: x_hat = s * H (n c[code]) / sqrt(d).
 //
-// A segment of d / ELEM lanes owns a vector, ELEM values per lane (16 bytes of input); the
-// Hadamard butterflies run inside a lane for strides below ELEM and across lanes above it.
+// A segment of d / 16 lanes owns a vector, 16 values per lane; only the Hadamard stages over
+// the lane bits of a channel index cross lanes (DPP quad permutes and ds_swizzle).  Decisions use
+// the codebook's antisymmetry (a 3-step binary search over the positive thresholds at 4 bits).
 // The codebook itself is computed on the host (fa_tq_codebook): Lloyd-Max iterations with the
 // cell masses and first moments of the Beta(d/2, d/2) law integrated by Gauss-Legendre
 // quadrature.
@@ -22,137 +23,236 @@
 namespace fa {
 namespace {
 
-constexpr int pow2_at_least(int r) { return r <= 1 ? 1 : 2 * pow2_at_least((r + 1) / 2); }
+// A segment of SEG = d/16 lanes owns a vector, 16 values per lane: NCH chunks of CE values
+// (16 bytes each), chunk j of lane sl being chunk sl + SEG j of the vector, so each 16-byte load
+// of a segment is one contiguous run.  Channel c = CE (sl + SEG j) + e: the Hadamard stages over
+// the bits of e and j stay inside the lane, the stages over the bits of sl cross lanes.
+template <int CE>
+struct Lay {
+  static constexpr int NCH = 16 / CE;
+};
 
-// in-place Walsh-Hadamard (Sylvester order) of the ELEM values of each lane and across the SEG
-// lanes of a segment: element index = ELEM * (lane % SEG) + e
-template <int ELEM, int SEG>
-__device__ __forceinline__ void hadamard_segment(float (&v)[ELEM], int lane) {
+// value of lane (lane ^ X) within aligned groups of X*2 lanes: DPP quad permutes for 1 and 2,
+// ds_swizzle (xor mode over 32 lanes) for 4 and 8
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int b = __float_as_int(v);
+  if constexpr (X == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
+  else if constexpr (X == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(b, (X << 10) | 0x1F));
+}
+
+// Butterfly across lanes l and l ^ X: with a on the lower lane and b on the upper, the lower takes
+// a + b and the upper a - b, both partner + g * own with g = +1 (lower) or -1 (upper).
+template <int X, int SEG>
+__device__ __forceinline__ void cross_stage(float (&v)[16], int sl) {
+  if constexpr (X < SEG) {
+    const float g = (sl & X) ? -1.f : 1.f;
 #pragma unroll
-  for (int h = 1; h < ELEM; h <<= 1)
-#pragma unroll
-    for (int e = 0; e < ELEM; ++e)
-      if ((e & h) == 0) {
-        const float a = v[e], b = v[e + h];
-        v[e] = a + b;
-        v[e + h] = a - b;
-      }
-#pragma unroll
-  for (int lh = 1; lh < SEG; lh <<= 1) {
-    const bool upper = lane & lh;
-#pragma unroll
-    for (int e = 0; e < ELEM; ++e) {
-      const float p = __shfl_xor(v[e], lh, 64);
-      v[e] = upper ? p - v[e] : v[e] + p;
-    }
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(g, v[i], lane_xor<X>(v[i]));
   }
+}
+
+template <int X, int SEG>
+__device__ __forceinline__ float cross_sum(float a) {
+  if constexpr (X < SEG) return a + lane_xor<X>(a);
+  return a;
+}
+
+// in-place Walsh-Hadamard (Sylvester order) over the d = 16 SEG values of a segment;
+// v[CE j + e] is channel CE (sl + SEG j) + e
+template <int CE, int SEG>
+__device__ __forceinline__ void hadamard16(float (&v)[16], int sl) {
+  constexpr int NCH = Lay<CE>::NCH;
+#pragma unroll
+  for (int h = 1; h < CE; h <<= 1)          // channel bits of e
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  cross_stage<1, SEG>(v, sl);                // channel bits of sl
+  cross_stage<2, SEG>(v, sl);
+  cross_stage<4, SEG>(v, sl);
+  cross_stage<8, SEG>(v, sl);
+#pragma unroll
+  for (int hj = 1; hj < NCH; hj <<= 1)      // channel bits of j
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (((i / CE) & hj) == 0) {
+        const float a = v[i], b = v[i + CE * hj];
+        v[i] = a + b;
+        v[i + CE * hj] = a - b;
+      }
 }
 
 template <int SEG>
 __device__ __forceinline__ float segment_sum(float a) {
-#pragma unroll
-  for (int o = SEG / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
-  return a;
+  a = cross_sum<1, SEG>(a);
+  a = cross_sum<2, SEG>(a);
+  a = cross_sum<4, SEG>(a);
+  return cross_sum<8, SEG>(a);
 }
+
+// The per-lane channel factors f[i] = sign(channel of v[i]) * scale.
+template <int CE, int SEG>
+__device__ __forceinline__ void channel_factors(float (&f)[16], const int8_t* signs, int sl, float scale) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = signs[CE * (sl + SEG * (i / CE)) + i % CE] < 0 ? -scale : scale;
+}
+
+// code = the number of thresholds <= u, for an antisymmetric codebook (thresholds t, with
+// t[h - 1] = 0 and positive thresholds tp[m] = t[h + m], h = 2^(bits-1)): u >= 0 gives
+// h + #{tp <= u}; u < 0 gives (h - 1) - #{tp < |u|}, and #{tp < |u|} is the <= count at the
+// float just below |u|.  With m = -1 for u < 0 (0 otherwise) both are (count ^ m) + h.  u must
+// not be -0.  At 4 bits the count over the 7 positive thresholds is a 3-step binary search.
+template <int BITS>
+__device__ __forceinline__ unsigned tq_code(float u, const float (&tp)[7]) {
+  constexpr int H = 1 << (BITS - 1);
+  const int ub = __float_as_int(u);
+  const int m = ub >> 31;
+  const float x = __int_as_float((ub & 0x7fffffff) + m);
+  int cnt;
+  if constexpr (BITS == 2) {
+    cnt = x >= tp[0] ? 1 : 0;
+  } else {
+    const bool c0 = x >= tp[3];
+    const float t1 = c0 ? tp[5] : tp[1];
+    const bool c1 = x >= t1;
+    const float hi = c1 ? tp[6] : tp[4];
+    const float lo = c1 ? tp[2] : tp[0];
+    const float t2 = c0 ? hi : lo;
+    cnt = (c0 ? 4 : 0) + (c1 ? 2 : 0) + (x >= t2 ? 1 : 0);
+  }
+  return (unsigned)((cnt ^ m) + H);
+}
+
+// Row groups (RPW rows, one per segment) a wave takes in turn; the channel factors are set up
+// once per wave.
+constexpr int kTqIter = 4;
 
 template <int D, bool BF16_IN, int BITS>
 __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
-  constexpr int ELEM = BF16_IN ? 8 : 4;
-  constexpr int SEG = D / ELEM;                // lanes per vector (power of two)
+  constexpr int CE = BF16_IN ? 8 : 4;        // values per 16-byte chunk
+  constexpr int NCH = 16 / CE;
+  constexpr int SEG = D / 16;                // lanes per vector
   constexpr int RPW = 64 / SEG;
-  constexpr int NT = (1 << BITS) - 1;          // thresholds
+  constexpr int CB = CE * BITS / 8;          // packed bytes per chunk
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
-  const int64_t row = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / SEG;
-  // every lane takes part in the butterflies: rows past the end repeat the last row
-  const int64_t r = min(row, a.n - 1);
-  float v[ELEM];
-  if constexpr (BF16_IN) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(a.x) + r * D + ELEM * sl);
+  float f[16];
+  channel_factors<CE, SEG>(f, a.signs, sl, 1.0f);
+  float tp[7];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = __uint_as_float(w[e] << 16);
-      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  for (int k = 0; k < 7; ++k) tp[k] = a.thr[(1 << (BITS - 1)) + (k < (1 << (BITS - 1)) - 1 ? k : 0)];
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
+  for (int it = 0; it < kTqIter; ++it) {
+    const int64_t row = (g0 + it) * RPW + lane / SEG;
+    if ((g0 + it) * RPW >= a.n) break;
+    // every lane takes part in the butterflies: rows past the end repeat the last row
+    const int64_t r = min(row, a.n - 1);
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int ch = sl + SEG * j;
+      if constexpr (BF16_IN) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(a.x) + r * D + CE * ch);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[CE * j + 2 * e] = __uint_as_float(w[e] << 16);
+          v[CE * j + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + r * D + CE * ch);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[CE * j + e] = w[e];
+      }
     }
-  } else {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + r * D + ELEM * sl);
+    float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = w[e];
-  }
-  float ss = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      ss = __builtin_fmaf(v[i], v[i], ss);
+      v[i] *= f[i];
+    }
+    const float n = __fsqrt_rn(segment_sum<SEG>(ss));
+    hadamard16<CE, SEG>(v, sl);
+    float yy = 0.f;
 #pragma unroll
-  for (int e = 0; e < ELEM; ++e) {
-    ss = __builtin_fmaf(v[e], v[e], ss);
-    v[e] = a.signs[ELEM * sl + e] < 0 ? -v[e] : v[e];
-  }
-  const float n = __fsqrt_rn(segment_sum<SEG>(ss));
-  hadamard_segment<ELEM, SEG>(v, lane);
-  float yy = 0.f;
+    for (int i = 0; i < 16; ++i) yy = __builtin_fmaf(v[i], v[i], yy);
+    const float ny = __fsqrt_rn(segment_sum<SEG>(yy));
+    const float inv = ny > 0.f ? __fdiv_rn(1.0f, ny) : 0.f;
+    if (row < a.n) {
 #pragma unroll
-  for (int e = 0; e < ELEM; ++e) yy = __builtin_fmaf(v[e], v[e], yy);
-  const float ny = __fsqrt_rn(segment_sum<SEG>(yy));
-  const float inv = ny > 0.f ? __fdiv_rn(1.0f, ny) : 0.f;
-  unsigned packed = 0;
+      for (int j = 0; j < NCH; ++j) {
+        unsigned packed = 0;
+        // fma with +0 rounds like the product and turns a -0 product into +0
 #pragma unroll
-  for (int e = 0; e < ELEM; ++e) {
-    const float u = v[e] * inv;
-    int code = 0;
-#pragma unroll
-    for (int k = 0; k < NT; ++k) code += u >= a.thr[k] ? 1 : 0;
-    packed |= (unsigned)code << (BITS * e);
-  }
-  if (row < a.n) {
-    uint8_t* dst = a.codes + row * (D * BITS / 8) + sl * (ELEM * BITS / 8);
-    if constexpr (ELEM * BITS == 32) *reinterpret_cast<unsigned*>(dst) = packed;
-    else if constexpr (ELEM * BITS == 16) *reinterpret_cast<unsigned short*>(dst) = (unsigned short)packed;
-    else *dst = (uint8_t)packed;
-    if (sl == 0) a.norms[row] = n;
+        for (int e = 0; e < CE; ++e)
+          packed |= tq_code<BITS>(__builtin_fmaf(v[CE * j + e], inv, 0.0f), tp) << (BITS * e);
+        uint8_t* dst = a.codes + row * (D * BITS / 8) + (sl + SEG * j) * CB;
+        if constexpr (CB == 4) *reinterpret_cast<unsigned*>(dst) = packed;
+        else if constexpr (CB == 2) *reinterpret_cast<unsigned short*>(dst) = (unsigned short)packed;
+        else *dst = (uint8_t)packed;
+      }
+      if (sl == 0) a.norms[row] = n;
+    }
   }
 }
 
 template <int D, bool BF16_OUT, int BITS>
 __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
-  constexpr int ELEM = 4;                      // fp32 values per lane
-  constexpr int SEG = D / ELEM;
+  constexpr int CE = 4;                       // fp32 values per chunk of the layout
+  constexpr int NCH = 4;
+  constexpr int SEG = D / 16;
   constexpr int RPW = 64 / SEG;
+  constexpr int CB = CE * BITS / 8;
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = a.cb[threadIdx.x];
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
-  const int64_t row = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / SEG;
-  const int64_t r = min(row, a.n - 1);
-  const uint8_t* src = a.codes + r * (D * BITS / 8) + sl * (ELEM * BITS / 8);
-  const unsigned packed = BITS == 4 ? *reinterpret_cast<const unsigned short*>(src) : *src;
-  const float n = a.norms[r];
-  float v[ELEM];
+  float f[16];
+  channel_factors<CE, SEG>(f, a.signs, sl, a.inv_sqrt_d);
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
+  for (int it = 0; it < kTqIter; ++it) {
+    const int64_t row = (g0 + it) * RPW + lane / SEG;
+    if ((g0 + it) * RPW >= a.n) break;
+    const int64_t r = min(row, a.n - 1);
+    const float n = a.norms[r];
+    float v[16];
 #pragma unroll
-  for (int e = 0; e < ELEM; ++e) {
-    const int code = (packed >> (BITS * e)) & ((1u << BITS) - 1);
-    float c = a.cb[0];
+    for (int j = 0; j < NCH; ++j) {
+      const uint8_t* src = a.codes + r * (D * BITS / 8) + (sl + SEG * j) * CB;
+      const unsigned packed = CB == 2 ? *reinterpret_cast<const unsigned short*>(src) : *src;
+      // rounded on its own: an fma with the first butterfly's add would round differently
 #pragma unroll
-    for (int k = 1; k < (1 << BITS); ++k) c = code == k ? a.cb[k] : c;
-    v[e] = n * c;
-  }
-  hadamard_segment<ELEM, SEG>(v, lane);
-  const float scale = a.inv_sqrt_d;
+      for (int e = 0; e < CE; ++e) v[CE * j + e] = mul_rn(n, cb[(packed >> (BITS * e)) & ((1u << BITS) - 1)]);
+    }
+    hadamard16<CE, SEG>(v, sl);
+    if (row < a.n) {
 #pragma unroll
-  for (int e = 0; e < ELEM; ++e) {
-    const float x = v[e] * scale;
-    v[e] = a.signs[ELEM * sl + e] < 0 ? -x : x;
-  }
-  if (row < a.n) {
-    if constexpr (BF16_OUT) {
-      const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + ELEM * sl) = w;
-    } else {
-      const f32x4 w = {v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + ELEM * sl) = w;
+      for (int j = 0; j < NCH; ++j) {
+        const int ch = sl + SEG * j;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = v[CE * j + e] * f[CE * j + e];
+        if constexpr (BF16_OUT) {
+          const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + CE * ch) = w;
+        } else {
+          const f32x4 w = {y[0], y[1], y[2], y[3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + CE * ch) = w;
+        }
+      }
     }
   }
 }
 
 template <int D, int BITS>
 hipError_t launch_encode_d(const TqArgs& a, bool bf16, hipStream_t st, const char** name) {
-  const int seg = D / (bf16 ? 8 : 4);
-  const int64_t rows_per_block = 4 * (64 / seg);
+  const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqIter;
   const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (bf16) hipLaunchKernelGGL((tq_encode_kernel<D, true, BITS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
@@ -163,7 +263,7 @@ hipError_t launch_encode_d(const TqArgs& a, bool bf16, hipStream_t st, const cha
 
 template <int D, int BITS>
 hipError_t launch_decode_d(const TqArgs& a, bool bf16_out, hipStream_t st, const char** name) {
-  const int64_t rows_per_block = 4 * (64 / (D / 4));
+  const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqIter;
   const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (bf16_out) hipLaunchKernelGGL((tq_decode_kernel<D, true, BITS>), dim3((unsigned)blocks), dim3(256), 0, st, a);

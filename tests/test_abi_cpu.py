@@ -228,5 +228,13 @@ def test_tq_rejects_bad_codebook_and_pointers(L):
     good = fa.tq_codebook(64, 2)
     assert L.fa_tq_encode(vp(1 << 20), 0, 4, 64, 2, vp(1 << 20), vp(bad.ctypes.data), vp(1 << 20), vp(1 << 20), None) == -1
     assert L.fa_tq_encode(vp(0), 0, 4, 64, 2, vp(1 << 20), vp(good.ctypes.data), vp(1 << 20), vp(1 << 20), None) == -1
+    # encode decides through the codebook's antisymmetry, so a shifted codebook is refused
+    shifted = (good + np.float32(0.01)).astype(np.float32)
+    assert L.fa_tq_encode(vp(1 << 20), 0, 4, 64, 2, vp(1 << 20), vp(shifted.ctypes.data), vp(1 << 20), vp(1 << 20), None) == -1
+    assert "antisymmetric" in fa.last_error()
+    for d in (32, 64, 128, 256):
+        for bits in (2, 4):
+            cb = fa.tq_codebook(d, bits)
+            assert np.array_equal(cb, -cb[::-1]), "the host codebook is not exactly antisymmetric"
     assert L.fa_tq_encode(vp(0), 0, 0, 64, 2, vp(0), vp(good.ctypes.data), vp(0), vp(0), None) == 0
     assert L.fa_tq_decode(vp(1 << 20), vp(1 << 20), 4, 64, 2, vp(1 << 20), vp(good.ctypes.data), vp(1 << 20), 2, None) == -2
