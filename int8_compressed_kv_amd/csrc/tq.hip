@@ -37,8 +37,8 @@ struct Lay {
 template <int X>
 __device__ __forceinline__ float lane_xor(float v) {
   const int b = __float_as_int(v);
-  if constexpr (X == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
-  else if constexpr (X == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
+  if constexpr (X == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+  else if constexpr (X == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
   else return __int_as_float(__builtin_amdgcn_ds_swizzle(b, (X << 10) | 0x1F));
 }
 
@@ -133,6 +133,14 @@ __device__ __forceinline__ unsigned tq_code(float u, const float (&tp)[7]) {
 // once per wave.
 constexpr int kTqIter = 4;
 
+// The NCH 16-byte chunks of row r a lane holds (chunk j = chunk sl + SEG j of the row).
+template <int ROW_BYTES, int SEG, int NCH>
+__device__ __forceinline__ void load_chunks(u32x4 (&w)[NCH], const void* x, int64_t r, int sl) {
+  const char* p = static_cast<const char*>(x) + r * ROW_BYTES + 16 * sl;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) w[j] = *reinterpret_cast<const u32x4*>(p + 16 * SEG * j);
+}
+
 template <int D, bool BF16_IN, int BITS>
 __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
   constexpr int CE = BF16_IN ? 8 : 4;        // values per 16-byte chunk
@@ -140,6 +148,7 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
   constexpr int SEG = D / 16;                // lanes per vector
   constexpr int RPW = 64 / SEG;
   constexpr int CB = CE * BITS / 8;          // packed bytes per chunk
+  constexpr int ROW_BYTES = D * (BF16_IN ? 2 : 4);
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
   float f[16];
@@ -148,26 +157,27 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
 #pragma unroll
   for (int k = 0; k < 7; ++k) tp[k] = a.thr[(1 << (BITS - 1)) + (k < (1 << (BITS - 1)) - 1 ? k : 0)];
   const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
+  // every lane takes part in the butterflies: rows past the end repeat the last row
+  u32x4 cur[NCH], nxt[NCH];
+  load_chunks<ROW_BYTES, SEG, NCH>(cur, a.x, min(g0 * RPW + lane / SEG, a.n - 1), sl);
+#pragma unroll
   for (int it = 0; it < kTqIter; ++it) {
-    const int64_t row = (g0 + it) * RPW + lane / SEG;
     if ((g0 + it) * RPW >= a.n) break;
-    // every lane takes part in the butterflies: rows past the end repeat the last row
-    const int64_t r = min(row, a.n - 1);
+    const int64_t row = (g0 + it) * RPW + lane / SEG;
+    // the next row group's loads go out before this one's arithmetic
+    if (it + 1 < kTqIter && (g0 + it + 1) * RPW < a.n)
+      load_chunks<ROW_BYTES, SEG, NCH>(nxt, a.x, min(row + RPW, a.n - 1), sl);
     float v[16];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ch = sl + SEG * j;
-      if constexpr (BF16_IN) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(a.x) + r * D + CE * ch);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[CE * j + 2 * e] = __uint_as_float(w[e] << 16);
-          v[CE * j + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16_IN) {
+          v[CE * j + 2 * e] = __uint_as_float(cur[j][e] << 16);
+          v[CE * j + 2 * e + 1] = __uint_as_float(cur[j][e] & 0xffff0000u);
+        } else {
+          v[CE * j + e] = __uint_as_float(cur[j][e]);
         }
-      } else {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + r * D + CE * ch);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[CE * j + e] = w[e];
       }
     }
     float ss = 0.f;
@@ -198,6 +208,8 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
       }
       if (sl == 0) a.norms[row] = n;
     }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
   }
 }
 
@@ -210,25 +222,35 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   constexpr int CB = CE * BITS / 8;
   __shared__ float cb[16];
   if (threadIdx.x < 16) cb[threadIdx.x] = a.cb[threadIdx.x];
-  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
-  float f[16];
-  channel_factors<CE, SEG>(f, a.signs, sl, a.inv_sqrt_d);
   const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
+  // all row groups' codes and norms are loaded up front (rows past the end repeat the last row)
+  unsigned pk[kTqIter][NCH];
+  float nn[kTqIter];
+#pragma unroll
   for (int it = 0; it < kTqIter; ++it) {
-    const int64_t row = (g0 + it) * RPW + lane / SEG;
-    if ((g0 + it) * RPW >= a.n) break;
-    const int64_t r = min(row, a.n - 1);
-    const float n = a.norms[r];
-    float v[16];
+    const int64_t r = min((g0 + it) * RPW + lane / SEG, a.n - 1);
+    nn[it] = a.norms[r];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const uint8_t* src = a.codes + r * (D * BITS / 8) + (sl + SEG * j) * CB;
-      const unsigned packed = CB == 2 ? *reinterpret_cast<const unsigned short*>(src) : *src;
+      pk[it][j] = CB == 2 ? *reinterpret_cast<const unsigned short*>(src) : *src;
+    }
+  }
+  float f[16];
+  channel_factors<CE, SEG>(f, a.signs, sl, a.inv_sqrt_d);
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kTqIter; ++it) {
+    if ((g0 + it) * RPW >= a.n) break;
+    const int64_t row = (g0 + it) * RPW + lane / SEG;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
       // rounded on its own: an fma with the first butterfly's add would round differently
 #pragma unroll
-      for (int e = 0; e < CE; ++e) v[CE * j + e] = mul_rn(n, cb[(packed >> (BITS * e)) & ((1u << BITS) - 1)]);
+      for (int e = 0; e < CE; ++e) v[CE * j + e] = mul_rn(nn[it], cb[(pk[it][j] >> (BITS * e)) & ((1u << BITS) - 1)]);
     }
     hadamard16<CE, SEG>(v, sl);
     if (row < a.n) {
