@@ -59,6 +59,7 @@ LEG_SOURCES = {
     "append": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
     "merge": ("merge.hip", "device_common.hpp", "kernel_args.hpp"),
     "tq": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
+    "tq_dec": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
