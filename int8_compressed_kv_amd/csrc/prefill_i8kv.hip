@@ -33,6 +33,8 @@
 //   * Tiles wholly outside a wave's causal / window band are skipped; element masks are
 //     applied only on boundary tiles.  Blocks run longest-first under causal masks and are
 //     dealt to the 8 XCDs so that the G query heads sharing a KV head stay on one XCD.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace fa {
@@ -63,29 +65,56 @@ __device__ __forceinline__ int swz(int r) {
   return (((r & 3) << 2) | ((r >> 2) & 3)) & (SWZ - 1);
 }
 
-__device__ __forceinline__ unsigned gather_byte(unsigned w0, unsigned w1, unsigned w2, unsigned w3, int b) {
-  const unsigned s = 8u * b;
-  return ((w0 >> s) & 0xffu) | (((w1 >> s) & 0xffu) << 8) | (((w2 >> s) & 0xffu) << 16) |
-         (((w3 >> s) & 0xffu) << 24);
+// Direct global -> LDS copies (no output registers: the data goes to LDS, so the compiler adds
+// no wait before later LDS reads; the kernel waits for its own copies before the barrier that
+// publishes them).  16 bytes per lane land at LDS byte address lds + 16 l, 4 bytes at lds + 4 l.
+__device__ __forceinline__ void copy16_to_lds(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(N) for N < 16, the other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
 }
 
 template <int D>
 __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(PrefillArgs a) {
   using C = Cfg<D>;
-  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, NST = 2, CH = C::CH;
+  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, CH = C::CH;
   constexpr int SWZ = C::SWZ;
   constexpr int NKS = D / 16;   // 16-deep k-steps of Q.K
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O
+  // head_dim 64 and 128: int8 tiles arrive by direct global -> LDS copies into four staging
+  // stages and are converted once per workgroup into the two operand stages; other head dims
+  // stage the codes through registers.
+  constexpr bool DMA = D == 64 || D == 128;
+  constexpr int SEGS = BN * D / 1024;              // 1-KiB segments of one int8 tile
+  constexpr int SPW = DMA ? 2 * SEGS / NW : 1;     // K and V segments copied per wave per tile
+  constexpr int NS8 = DMA ? 4 : 1;
+  constexpr int Q8 = DMA ? 2 * BN * D : 16;        // bytes per staging stage: K codes, then V codes
 
-  __shared__ __attribute__((aligned(16))) unsigned short lds_k[NST][C::TILE];
-  __shared__ __attribute__((aligned(16))) unsigned short lds_v[NST][C::TILE];
-  __shared__ __attribute__((aligned(16))) float lds_ks[NST][BN];
-  __shared__ __attribute__((aligned(16))) float lds_vs[NST][BN];
+  __shared__ __attribute__((aligned(16))) unsigned short lds_k[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) unsigned short lds_v[2][C::TILE];
+  __shared__ __attribute__((aligned(16))) float lds_ks[2][BN];
+  __shared__ __attribute__((aligned(16))) float lds_vs[2][BN];
+  __shared__ __attribute__((aligned(16))) int8_t lds_q8[NS8][Q8];
+  __shared__ __attribute__((aligned(16))) float lds_s8[NS8][DMA ? 2 * BN : 4];
   __shared__ float lds_red[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   const int h = lane >> 5;       // half of the wave (MFMA k-slot group)
   const int c = lane & 31;       // MFMA column (query) / row (key, head-dim)
   const int g16 = lane >> 4;     // 16-lane group of the transposing reads
@@ -139,7 +168,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   vs_norm = ldexpf(1.f, -e);
   vs_unnorm = ldexpf(1.f, e);
 
-
   // ---- Q fragments (B operand of S^T): Qf[ks] = Q[qw0 + c][16 ks + 8 h .. + 8]
   const int qw0 = q0 + 32 * wave;
   const int qi = qw0 + c;
@@ -156,59 +184,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
   const int last_key = a.s_k - 1;
 
-  // ---- staging: tile rows k0 .. k0 + 63 are read as 8-byte chunks of codes with buffer loads
-  // (a scalar resource per tile, based at row k0 and ending at the head's last key, plus a
-  // constant per-lane offset; rows past the end read as zero and are masked in the softmax),
-  // double-buffered in registers, converted exactly (K -> bf16, V -> fp16) and written to LDS at
-  // row r, physical chunk lc ^ swz(r).  Waves 0 and 1 also fetch the tile's k and v scales.
-  u32x2 kreg[CH], vreg[CH];
-  int soff[CH];
-#pragma unroll
-  for (int u = 0; u < CH; ++u) {
-    const int idx = min(tid + 64 * NW * u, BN * NC - 1);
-    soff[u] = (idx / NC) * D + 8 * (idx % NC);
-  }
-  const float* scale_src = (wave & 1) ? a.v_scale : a.k_scale;
-  const float scale_mul = (wave & 1) ? vs_norm : 1.f;
-  float sreg = 0.f;
-  auto load_tile = [&](int t) {
-    const int k0 = (t_lo + t) * BN;
-    const int64_t rem = (int64_t)(a.s_k - k0) * D;
-    const int nrec = (int)(rem < 0x7fffffff ? rem : 0x7fffffff);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kp8 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(vp8 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      kreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, soff[u], 0, 0));
-      vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, soff[u], 0, 0));
-    }
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(scale_src + kv_base + k0), 0, (a.s_k - k0) * 4, kBufferFlags);
-    sreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0)) * scale_mul;
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = tid + 64 * NW * u;
-      if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
-        const int r = idx / NC, lc = idx % NC;
-        const int pc = lc ^ swz<SWZ>(r);
-        const u32x2 k0v = i8x4_to_bf16x4(kreg[u][0]), k1v = i8x4_to_bf16x4(kreg[u][1]);
-        const u32x2 v0v = i8x4_to_f16x4(vreg[u][0]), v1v = i8x4_to_f16x4(vreg[u][1]);
-        const u32x4 kw = {k0v[0], k0v[1], k1v[0], k1v[1]};
-        const u32x4 vw = {v0v[0], v0v[1], v1v[0], v1v[1]};
-        *reinterpret_cast<u32x4*>(lds_k[st] + r * D + 8 * pc) = kw;
-        *reinterpret_cast<u32x4*>(lds_v[st] + r * D + 8 * pc) = vw;
-      }
-    }
-    if (tid < 2 * BN) {
-      if (tid < BN) lds_ks[st][tid] = sreg;
-      else lds_vs[st][tid - BN] = sreg;
-    }
-  };
-
   // ---- per-wave state
   f32x16 O[NDB];
 #pragma unroll
@@ -221,132 +196,327 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   const int w_last = qw0 + 31;
   const bool wave_live = qw0 < a.s_q;
 
-  // ---- pipeline: the global loads of tile t+1 are in flight while tile t is computed
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // V^T fragments of 32-key half kb of a tile: vf[s2][db] holds keys kbase + 0..3 and
+  // kbase + 8 + 0..3 (kbase = 32 kb + 16 s2 + 4 h) of head-dim 32 db + c, from two transposing
+  // LDS reads of the row-major tile
+  auto vread = [&](const unsigned short* Vt, int kb, u32x4 (&vf)[2][NDB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
+        const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
+        const s16x4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0));
+        const s16x4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+        vf[s2][db] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+      }
+    }
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-
+  // one tile from operand stage `stage` (K bf16, V fp16, k_s, v_s 2^-E)
+  auto compute = [&](const int t, auto stage) __attribute__((always_inline)) {
+    const int st = static_cast<int>(stage);
     const int k0 = (t_lo + t) * BN;
     bool skip = !wave_live;
     if (a.causal && k0 > w_last + off) skip = true;
     if (a.window && k0 + BN - 1 <= qw0 + off - a.window) skip = true;
-    if (!skip) {
-      const bool need_mask = (k0 + BN > a.s_k) || (a.causal && k0 + BN - 1 > qw0 + off) ||
-                             (a.window && k0 <= w_last + off - a.window);
-      const unsigned short* Kt = lds_k[st];
-      const unsigned short* Vt = lds_v[st];
+    if (skip) return;
+    const bool need_mask = (k0 + BN > a.s_k) || (a.causal && k0 + BN - 1 > qw0 + off) ||
+                           (a.window && k0 <= w_last + off - a.window);
+    const unsigned short* Kt = lds_k[st];
+    const unsigned short* Vt = lds_v[st];
 
+    // S^T of both 32-key halves, two independent MFMA chains: S[kb] lane (c, h) element i holds
+    // key 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative) of query qi
+    f32x16 S[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T: lane holds keys 32 kb + 8 (i/4) + 4 h + i%4 (tile-relative) for query qi
-        bf16x8 kf[NKS];
         const int krow = 32 * kb + c;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          kf[ks] = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
-        f32x16 S;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) S = mfma32_bf16(kf[ks], Qf[ks], S);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
+        S[kb] = mfma32_bf16(kf, Qf[ks], S[kb]);
+      }
 
-        // V^T fragments for this 32-key step: vf[s2][db] holds keys kbase + 0..3 and
-        // kbase + 8 + 0..3 (kbase = 32 kb + 16 s2 + 4 h) of head-dim 32 db + c
-        u32x4 vf[2][NDB];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-            const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
-            const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
-            const s16x4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0));
-            const s16x4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1));
-            const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
-            vf[s2][db] = u32x4{w0[0], w0[1], w1[0], w1[1]};
-          }
-        }
+    // V^T fragments of the first 32 keys, read while the softmax runs
+    u32x4 vf0[2][NDB];
+    vread(Vt, 0, vf0);
 
+    // k_s scales the scores of each key
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[st][32 * kb + 8 * g4 + 4 * h]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) S[4 * g4 + e] *= sc[e];
-        }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[st][32 * kb + 8 * g4 + 4 * h]);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) S[kb][4 * g4 + e2] *= sc[e2];
+      }
 
-        if (need_mask) {
-          // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
-          const int kl0 = k0 + 32 * kb + 4 * h;
-          int hi_i = a.s_k - 1 - kl0;
-          if (a.causal) hi_i = min(hi_i, qi + off - kl0);
-          int lo_i = a.window ? qi + off - a.window + 1 - kl0 : -0x40000000;
+    if (need_mask) {
+      // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ko = 8 * (i / 4) + (i % 4);
-            if (ko > hi_i || ko < lo_i) S[i] = neg_inf();
-          }
-        }
-
-        // online softmax with a lazily raised max
-        float mx = neg_inf();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-        mx = max_xor32(mx);
-        if (__any(mx - m_run > lazy_thr)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-          const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
-          m_run = m_new;
-          mc = m_use * c2;
-        }
-        float p[16];
-        float ps = 0.f;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kl0 = k0 + 32 * kb + 4 * h;
+        int hi_i = a.s_k - 1 - kl0;
+        if (a.causal) hi_i = min(hi_i, qi + off - kl0);
+        const int lo_i = a.window ? qi + off - a.window + 1 - kl0 : -0x40000000;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -mc));
-          ps += p[i];
+          const int ko = 8 * (i / 4) + (i % 4);
+          if (ko > hi_i || ko < lo_i) S[kb][i] = neg_inf();
         }
-        l_run += ps;
-        // P^T as B operands: k-step s2 takes p[8 s2 .. 8 s2 + 7]
-        u32x4 Pw[2];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[st][32 * kb + 8 * g4 + 4 * h]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[4 * g4 + e] *= sc[e];
-        }
-#pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) Pw[q2 / 4][q2 % 4] = pack_f16x2(p[2 * q2], p[2 * q2 + 1]);
-
-        // O^T[db] += V^T P^T
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf[s2][db]), __builtin_bit_cast(f16x8, Pw[s2]), O[db]);
-          }
       }
     }
 
-    if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
+    // online softmax over the tile's 64 keys with a lazily raised max
+    float mx2 = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx2 = fmaxf(mx2, S[kb][i]);
+    mx2 = max_xor32(mx2);
+    if (__any(mx2 - m_run > lazy_thr)) {
+      const float m_new = fmaxf(m_run, mx2);
+      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+      m_run = m_new;
+      mc = m_use * c2;
+    }
+    // P^T (times v_s 2^-E, in fp16) as B operands: k-step (kb, s2) takes S[kb][8 s2 .. 8 s2 + 7].
+    // The row sum adds the fp32 exponentials as a tree, so l is their exact fp32 sum.
+    u32x4 Pw[2][2];
+    float lpair[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[st][32 * kb + 8 * g4 + 4 * h]);
+        float p[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) p[e2] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g4 + e2], c2, -mc));
+        lpair[8 * kb + 2 * g4] = p[0] + p[1];
+        lpair[8 * kb + 2 * g4 + 1] = p[2] + p[3];
+        Pw[kb][g4 / 2][2 * (g4 % 2)] = pack_f16x2(p[0] * sc[0], p[1] * sc[1]);
+        Pw[kb][g4 / 2][2 * (g4 % 2) + 1] = pack_f16x2(p[2] * sc[2], p[3] * sc[3]);
+      }
+#pragma unroll
+    for (int st2 = 8; st2 >= 1; st2 >>= 1)
+#pragma unroll
+      for (int j = 0; j < st2; ++j) lpair[j] += lpair[j + st2];
+    l_run += lpair[0];
+
+    // O^T[db] += V^T P^T
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf0[s2][db]), __builtin_bit_cast(f16x8, Pw[0][s2]), O[db]);
+    u32x4 vf1[2][NDB];
+    vread(Vt, 1, vf1);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf1[s2][db]), __builtin_bit_cast(f16x8, Pw[1][s2]), O[db]);
+  };
+
+  // converted 16-byte chunk (8 values) of row r, logical chunk lc, into operand stage st
+  auto put_chunks = [&](unsigned short* dst, int r, int lc, u32x4 w) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4*>(dst + r * D + 8 * (lc ^ swz<SWZ>(r))) = w;
+  };
+
+  if constexpr (DMA) {
+    // Per tile: wave w copies K/V segments SPW w .. SPW w + SPW - 1 (segment gs < SEGS is K
+    // segment gs, else V segment gs - SEGS; lane l of a segment brings the 16 codes at byte
+    // 1024 seg + 16 l of the row-major tile), wave 0 the 64 k scales and wave 1 the 64 v scales.
+    // Tile t + 3's copies are issued after tile t is computed and converted-ahead, so after the
+    // barrier that ended the conversion of tile t - 1 (the last reader of that staging stage),
+    // and waited for at the end of iteration t + 2.
+    const unsigned q8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int8_t*)&lds_q8[0][0];
+    const unsigned s8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)&lds_s8[0][0];
+    int crow[SPW], ccol[SPW];
+    unsigned voff[SPW], seg_lds[SPW];
+    const int8_t* cbase[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int gs = SPW * wave + j;
+      const int mat = gs / SEGS, seg = gs % SEGS;
+      const int p = 1024 * seg + 16 * lane;
+      crow[j] = p / D;
+      ccol[j] = p % D;
+      voff[j] = (unsigned)p;
+      cbase[j] = mat ? vp8 : kp8;
+      seg_lds[j] = __builtin_amdgcn_readfirstlane(q8_0 + (unsigned)(mat * BN * D + 1024 * seg));
+    }
+    const float* sc_src = wave == 0 ? a.k_scale : a.v_scale;
+    const unsigned sc_lds = s8_0 + (wave == 0 ? 0u : 4u * BN);
+    auto copy_tile = [&](int t) __attribute__((always_inline)) {
+      const int k0 = (t_lo + t) * BN;
+      const unsigned st_off = (unsigned)(Q8 * (t % NS8));
+      if (k0 + BN <= a.s_k) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) copy16_to_lds(cbase[j] + (int64_t)k0 * D, voff[j], seg_lds[j] + st_off);
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
+          copy16_to_lds(cbase[j] + row * D + ccol[j], seg_lds[j] + st_off);
+        }
+      }
+      if (wave < 2)
+        copy4_to_lds(sc_src + kv_base + min(k0 + lane, last_key), sc_lds + (unsigned)(4 * 2 * BN * (t % NS8)));
+    };
+    // the copies of the latest tile may stay in flight; those of the one before must have landed
+    auto wait_all_but_latest = [&]() __attribute__((always_inline)) {
+      if (wave < 2) wait_vmcnt<SPW + 1>();
+      else wait_vmcnt<SPW>();
+    };
+    // staging stage s8 -> operand stage st: thread tid converts chunk tid + 64 NW u of the 2 BN D / 16
+    // chunks (K chunks first); threads 0 .. 2 BN - 1 move the scales (v_s times 2^-E)
+    auto convert = [&](auto s8, auto stage) __attribute__((always_inline)) {
+      constexpr int NCH8 = 2 * BN * D / 16;
+#pragma unroll
+      for (int u = 0; u < NCH8 / (64 * NW); ++u) {
+        const int ci = tid + 64 * NW * u;
+        const bool is_v = ci >= NCH8 / 2;
+        const int cm = is_v ? ci - NCH8 / 2 : ci;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&lds_q8[static_cast<int>(s8)][16 * ci]);
+        const int r = (16 * cm) / D, lc = 2 * ((16 * cm) % D / 16);
+        if (is_v) {
+          const u32x2 x0 = i8x4_to_f16x4(w[0]), x1 = i8x4_to_f16x4(w[1]);
+          const u32x2 x2 = i8x4_to_f16x4(w[2]), x3 = i8x4_to_f16x4(w[3]);
+          put_chunks(lds_v[static_cast<int>(stage)], r, lc, u32x4{x0[0], x0[1], x1[0], x1[1]});
+          put_chunks(lds_v[static_cast<int>(stage)], r, lc + 1, u32x4{x2[0], x2[1], x3[0], x3[1]});
+        } else {
+          const u32x2 x0 = i8x4_to_bf16x4(w[0]), x1 = i8x4_to_bf16x4(w[1]);
+          const u32x2 x2 = i8x4_to_bf16x4(w[2]), x3 = i8x4_to_bf16x4(w[3]);
+          put_chunks(lds_k[static_cast<int>(stage)], r, lc, u32x4{x0[0], x0[1], x1[0], x1[1]});
+          put_chunks(lds_k[static_cast<int>(stage)], r, lc + 1, u32x4{x2[0], x2[1], x3[0], x3[1]});
+        }
+      }
+      if (tid < 2 * BN) {
+        const float sv = lds_s8[static_cast<int>(s8)][tid];
+        if (tid < BN) lds_ks[static_cast<int>(stage)][tid] = sv;
+        else lds_vs[static_cast<int>(stage)][tid - BN] = sv * vs_norm;
+      }
+    };
+    // iteration t: compute tile t, convert tile t + 1, copy tile t + 3, wait for tile t + 2, barrier
+    auto iter = [&](int t, auto st, auto st1, auto s81) __attribute__((always_inline)) {
+      if (t >= n_tiles) return;
+      compute(t, st);
+      if (t + 1 < n_tiles) convert(s81, st1);
+      if (t + 3 < n_tiles) {
+        copy_tile(t + 3);
+        wait_all_but_latest();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+    };
+    if (n_tiles > 0) {
+      copy_tile(0);
+      wait_vmcnt<0>();
+      __syncthreads();
+      convert(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      if (n_tiles > 1) copy_tile(1);
+      if (n_tiles > 2) {
+        copy_tile(2);
+        wait_all_but_latest();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+    }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int t = 0; t < n_tiles; t += 4) {
+      iter(t, I0{}, I1{}, I1{});
+      iter(t + 1, I1{}, I0{}, I2{});
+      iter(t + 2, I0{}, I1{}, I3{});
+      iter(t + 3, I1{}, I0{}, I0{});
+    }
+  } else {
+    // ---- staging through registers: tile rows k0 .. k0 + 63 are read as 8-byte chunks of codes
+    // with buffer loads (a scalar resource per tile, based at row k0 and ending at the head's last
+    // key, plus a constant per-lane offset; rows past the end read as zero and are masked in the
+    // softmax), double-buffered in registers, converted exactly (K -> bf16, V -> fp16) and written
+    // to LDS at row r, physical chunk lc ^ swz(r).  Waves 0 and 1 also fetch the tile's scales.
+    u32x2 kreg[CH], vreg[CH];
+    int soff[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = min(tid + 64 * NW * u, BN * NC - 1);
+      soff[u] = (idx / NC) * D + 8 * (idx % NC);
+    }
+    const float* scale_src = (wave & 1) ? a.v_scale : a.k_scale;
+    const float scale_mul = (wave & 1) ? vs_norm : 1.f;
+    float sreg = 0.f;
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
+      const int k0 = (t_lo + t) * BN;
+      const int64_t rem = (int64_t)(a.s_k - k0) * D;
+      const int nrec = (int)(rem < 0x7fffffff ? rem : 0x7fffffff);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kp8 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(vp8 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        kreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, soff[u], 0, 0));
+        vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, soff[u], 0, 0));
+      }
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(scale_src + kv_base + k0), 0, (a.s_k - k0) * 4, kBufferFlags);
+      sreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0)) * scale_mul;
+    };
+    auto store_tile = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int idx = tid + 64 * NW * u;
+        if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
+          const int r = idx / NC, lc = idx % NC;
+          const u32x2 k0v = i8x4_to_bf16x4(kreg[u][0]), k1v = i8x4_to_bf16x4(kreg[u][1]);
+          const u32x2 v0v = i8x4_to_f16x4(vreg[u][0]), v1v = i8x4_to_f16x4(vreg[u][1]);
+          put_chunks(lds_k[st], r, lc, u32x4{k0v[0], k0v[1], k1v[0], k1v[1]});
+          put_chunks(lds_v[st], r, lc, u32x4{v0v[0], v0v[1], v1v[0], v1v[1]});
+        }
+      }
+      if (tid < 2 * BN) {
+        if (tid < BN) lds_ks[st][tid] = sreg;
+        else lds_vs[st][tid - BN] = sreg;
+      }
+    };
+    // the global loads of tile t+1 are in flight while tile t is computed
+    if (n_tiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
     __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int st = t & 1;
+      if (t + 1 < n_tiles) load_tile(t + 1);
+      compute(t, st);
+      if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
+      __syncthreads();
+    }
   }
 
-  // ---- finalize: O / l (x 2^E for int8), epilogue, store; LSE = sigma m + ln l
+  // ---- finalize: O / l x 2^E, epilogue, store; LSE = sigma m + ln l
   const float l_tot = add_xor32(l_run);
   float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
   inv *= vs_unnorm;
