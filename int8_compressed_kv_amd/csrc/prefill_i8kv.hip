@@ -5,31 +5,33 @@
 // PR, Summary: FA-2 forward, fp32 accumulation, compressed int8 KV dequantized inside q.k and
 // p.v; Foundry attention/ README, References: the online-softmax recurrence).  For each key
 // tile, with running row max m, running sum l and accumulator O:
-//   S = sigma * k_s Q K~^T (masked) ; m' = max(m, rowmax S) ; P = exp(S - m') ;
-//   l = exp(m - m') l + rowsum P ; O = exp(m - m') O + (P v_s) V~.
+//   S = sigma Q (k_s K8)^T (masked) ; m' = max(m, rowmax S) ; P = exp(S - m') ;
+//   l = exp(m - m') l + rowsum P ; O = exp(m - m') O + P (v_s V8).
 // Finally O / l, the epilogue ops in fp32, and the store.
 //
 // gfx950 mapping
 //   * A workgroup is 8 waves = 256 query rows (4 waves for head_dim > 128, whose fragments
 //     need the whole register file); each wave owns 32 rows and keeps their Q fragments in
-//     registers.  Two waves per SIMD: while one runs the softmax on the vector ALU the other
-//     keeps the matrix core busy.
-//   * The int8 codes are converted exactly to bf16 (K) and fp16 (V) on their way from the
-//     staging registers into LDS -- the compressed cache is never expanded in global memory.
-//     K and V tiles of 64 keys live in LDS row-major, 16-byte chunks XOR-swizzled by row so
-//     that both operand reads below are free of bank conflicts.  Tiles are double-buffered:
-//     the global loads of tile t+1 are in flight (in registers) while tile t is computed, then
-//     converted and written to the other LDS stage; one barrier per tile.
-//   * S^T = K Q^T (keys = MFMA rows, queries = columns) on v_mfma_f32_32x32x16_bf16: each
-//     query's scores sit in one lane pair, so the row max needs one exchange; k_s scales S in
-//     registers.  P~^T = fp16(P v_s 2^-E) in the accumulator layout is the B operand of
-//     O^T += V~^T P~^T on v_mfma_f32_32x32x16_f16; E is a power of two from the largest v_s
-//     the block visits (keeps P v_s in fp16 range) and O is multiplied back by 2^E at the end.
-//     The V~^T operand (8 keys of one head-dim column per lane) comes from two transposing
-//     LDS reads (ds_read_b64_tr_b16) of the row-major tile.
+//     registers.
+//   * Dequantization happens once per workgroup and tile, on the way into the operand tiles in
+//     LDS: K~ = fp16(k) * fp16(k_s 2^-Ek) and V~ = fp16(v) * fp16(v_s 2^-Ev) (codes are exact in
+//     fp16; one packed fp16 multiply per pair), where 2^-Ek, 2^-Ev put the block's largest scale
+//     in [128, 256).  Q is held in fp16 as Q 2^-Eq with the row's largest |q| in [2^14, 2^15)
+//     (bf16 -> fp16 exact there); the row's exp2-domain factor absorbs 2^(Eq + Ek), and O is
+//     multiplied by 2^Ev at the end.  The compressed cache is never expanded in global memory.
+//   * head_dim 64 / 128: the codes and scales of a tile are copied global -> LDS directly into
+//     four staging stages (tile t + 3 in flight while tile t is computed) and converted into two
+//     operand stages; other head dims stage the codes through registers.  One barrier per tile.
+//   * Operand tiles of 64 keys are row-major in LDS, 16-byte chunks XOR-swizzled by row so that
+//     both operand reads below are free of bank conflicts.
+//   * S^T = K~ Q~^T (keys = MFMA rows, queries = columns) on v_mfma_f32_32x32x16_f16: each
+//     query's scores sit in one lane pair, so the row max needs one exchange, and P^T (fp16) in
+//     the accumulator layout is already the B operand of O^T += V~^T P^T.  The V~^T operand
+//     (8 keys of one head-dim column per lane) comes from two transposing LDS reads
+//     (ds_read_b64_tr_b16) of the row-major tile.
 //   * The running max is only raised when a row's tile max exceeds it by more than 2^8 in the
 //     exp2 domain; otherwise the stale max is kept (O and l stay mutually consistent, the O
-//     rescale is skipped) and P stays below 2^8.
+//     rescale is skipped) and P stays below 2^8, inside fp16.
 //   * Tiles wholly outside a wave's causal / window band are skipped; element masks are
 //     applied only on boundary tiles.  Blocks run longest-first under causal masks and are
 //     dealt to the 8 XCDs so that the G query heads sharing a KV head stay on one XCD.
@@ -106,11 +108,9 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
 
   __shared__ __attribute__((aligned(16))) unsigned short lds_k[2][C::TILE];
   __shared__ __attribute__((aligned(16))) unsigned short lds_v[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) float lds_ks[2][BN];
-  __shared__ __attribute__((aligned(16))) float lds_vs[2][BN];
   __shared__ __attribute__((aligned(16))) int8_t lds_q8[NS8][Q8];
   __shared__ __attribute__((aligned(16))) float lds_s8[NS8][DMA ? 2 * BN : 4];
-  __shared__ float lds_red[NW];
+  __shared__ float lds_red[2][NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,33 +152,75 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   const int n_tiles = hi > lo ? (hi + BN - 1) / BN - t_lo : 0;
   const int64_t kv_base = (int64_t)kvh * a.s_k;
 
-  // ---- int8: power-of-two normalisation for P * v_s (largest v_s over [lo, hi))
-  float vs_norm = 1.f, vs_unnorm = 1.f;
-  float mx = 0.f;
-  for (int j = lo + tid; j < hi; j += 64 * NW) mx = fmaxf(mx, a.v_scale[kv_base + j]);
+  // ---- int8: power-of-two normalisers of the block's scales.  K~ = fp16(k) * fp16(k_s 2^-Ek) and
+  // V~ = fp16(v) * fp16(v_s 2^-Ev), with 2^-Ek, 2^-Ev putting the largest scale over the keys of
+  // the block's tiles in [128, 256), so that every |K~|, |V~| <= 127 * 256 stays inside fp16
+  // (also on masked keys, whose P = 0 must not meet an infinite V~)
+  float mk = 0.f, mv = 0.f;
+  const int key_end = min(a.s_k, (t_lo + n_tiles) * BN);
+  for (int j = t_lo * BN + tid; j < key_end; j += 64 * NW) {
+    mk = fmaxf(mk, a.k_scale[kv_base + j]);
+    mv = fmaxf(mv, a.v_scale[kv_base + j]);
+  }
 #pragma unroll
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
-  if (lane == 0) lds_red[wave] = mx;
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, o2, 64));
+    mv = fmaxf(mv, __shfl_xor(mv, o2, 64));
+  }
+  if (lane == 0) {
+    lds_red[0][wave] = mk;
+    lds_red[1][wave] = mv;
+  }
   __syncthreads();
-  mx = 0.f;
+  mk = 0.f;
+  mv = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_red[w]);
-  int e = 0;
-  if (mx > 0.f) (void)frexpf(mx, &e);   // mx = f * 2^e, f in [0.5, 1)
-  vs_norm = ldexpf(1.f, -e);
-  vs_unnorm = ldexpf(1.f, e);
+  for (int w = 0; w < NW; ++w) {
+    mk = fmaxf(mk, lds_red[0][w]);
+    mv = fmaxf(mv, lds_red[1][w]);
+  }
+  int ek = 0, ev = 0;
+  if (mk > 0.f) (void)frexpf(mk, &ek);   // mk = f * 2^ek, f in [0.5, 1)
+  if (mv > 0.f) (void)frexpf(mv, &ev);
+  ek = max(ek, -60);
+  ev = max(ev, -60);
+  const float ks_norm = ldexpf(1.f, 8 - ek);
+  const float vs_norm = ldexpf(1.f, 8 - ev);
+  const float vs_unnorm = ldexpf(1.f, ev - 8);
 
-  // ---- Q fragments (B operand of S^T): Qf[ks] = Q[qw0 + c][16 ks + 8 h .. + 8]
+  // ---- Q fragments (B operand of S^T) in fp16: Qf[ks] = Q~[qw0 + c][16 ks + 8 h .. + 8], Q~ = Q 2^-Eq
+  // with 2^-Eq putting the row's largest |q| in [2^14, 2^15) (bf16 -> fp16 is then exact down to
+  // 2^-28 of that largest value).  S~ = Q~ K~^T is S / (2^-Eq 2^-Ek): the row's exp2-domain factor
+  // c2row absorbs both powers of two.
   const int qw0 = q0 + 32 * wave;
   const int qi = qw0 + c;
   const unsigned short* qp = static_cast<const unsigned short*>(a.q) + (int64_t)head * a.s_q * D;
-  bf16x8 Qf[NKS];
+  u32x4 qraw[NKS];
+  float qmax = 0.f;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qi < a.s_q) w = *reinterpret_cast<const u32x4*>(qp + (int64_t)qi * D + 16 * ks + 8 * h);
-    Qf[ks] = __builtin_bit_cast(bf16x8, w);
+    qraw[ks] = u32x4{0u, 0u, 0u, 0u};
+    if (qi < a.s_q) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + (int64_t)qi * D + 16 * ks + 8 * h);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      qmax = fmaxf(qmax, fmaxf(fabsf(__uint_as_float(qraw[ks][e2] << 16)), fabsf(__uint_as_float(qraw[ks][e2] & 0xffff0000u))));
   }
+  qmax = max_xor32(qmax);
+  int eq = 0;
+  if (qmax > 0.f) (void)frexpf(qmax, &eq);
+  eq = max(eq, -60);
+  const float q_norm = ldexpf(1.f, 15 - eq);
+  f16x8 Qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    u32x4 w;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      w[e2] = pack_f16x2(__uint_as_float(qraw[ks][e2] << 16) * q_norm, __uint_as_float(qraw[ks][e2] & 0xffff0000u) * q_norm);
+    Qf[ks] = __builtin_bit_cast(f16x8, w);
+  }
+  // S = S~ 2^(eq - 15) 2^(ek - 8)
+  const int es = (eq - 15) + (ek - 8);
 
   const int8_t* kp8 = static_cast<const int8_t*>(a.k) + kv_base * D;
   const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
@@ -190,9 +232,9 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
-  float m_run = neg_inf(), l_run = 0.f, mc = 0.f;
-  const float c2 = a.scale_log2;
-  const float lazy_thr = C::kLazyLog2 / c2;   // raw-score headroom before the max is raised
+  float m_run = neg_inf(), l_run = 0.f, mc = 0.f;   // m_run in units of S~
+  const float c2 = ldexpf(a.scale_log2, es);       // exp2-domain factor of S~ for this row
+  const float lazy_thr = C::kLazyLog2 / c2;        // S~ headroom before the max is raised
   const int w_last = qw0 + 31;
   const bool wave_live = qw0 < a.s_q;
 
@@ -218,7 +260,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     }
   };
 
-  // one tile from operand stage `stage` (K bf16, V fp16, k_s, v_s 2^-E)
+  // one tile from operand stage `stage` (K~, V~ in fp16)
   auto compute = [&](const int t, auto stage) __attribute__((always_inline)) {
     const int st = static_cast<int>(stage);
     const int k0 = (t_lo + t) * BN;
@@ -243,23 +285,13 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int krow = 32 * kb + c;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
-        S[kb] = mfma32_bf16(kf, Qf[ks], S[kb]);
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(Kt + krow * D + 8 * ((2 * ks + h) ^ swz<SWZ>(krow)));
+        S[kb] = mfma32_f16(kf, Qf[ks], S[kb]);
       }
 
     // V^T fragments of the first 32 keys, read while the softmax runs
     u32x4 vf0[2][NDB];
     vread(Vt, 0, vf0);
-
-    // k_s scales the scores of each key
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_ks[st][32 * kb + 8 * g4 + 4 * h]);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) S[kb][4 * g4 + e2] *= sc[e2];
-      }
 
     if (need_mask) {
       // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
@@ -296,22 +328,18 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
       m_run = m_new;
       mc = m_use * c2;
     }
-    // P^T (times v_s 2^-E, in fp16) as B operands: k-step (kb, s2) takes S[kb][8 s2 .. 8 s2 + 7].
-    // The row sum adds the fp32 exponentials as a tree, so l is their exact fp32 sum.
+    // P^T in fp16 as B operands: k-step (kb, s2) takes S[kb][8 s2 .. 8 s2 + 7].  The row sum adds
+    // the fp32 exponentials as a tree, so l is their exact fp32 sum.
     u32x4 Pw[2][2];
     float lpair[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&lds_vs[st][32 * kb + 8 * g4 + 4 * h]);
-        float p[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) p[e2] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g4 + e2], c2, -mc));
-        lpair[8 * kb + 2 * g4] = p[0] + p[1];
-        lpair[8 * kb + 2 * g4 + 1] = p[2] + p[3];
-        Pw[kb][g4 / 2][2 * (g4 % 2)] = pack_f16x2(p[0] * sc[0], p[1] * sc[1]);
-        Pw[kb][g4 / 2][2 * (g4 % 2) + 1] = pack_f16x2(p[2] * sc[2], p[3] * sc[3]);
+      for (int q2 = 0; q2 < 8; ++q2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][2 * q2], c2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][2 * q2 + 1], c2, -mc));
+        Pw[kb][q2 / 4][q2 % 4] = pack_f16x2(p0, p1);
+        lpair[kb * 8 + q2] = p0 + p1;
       }
 #pragma unroll
     for (int st2 = 8; st2 >= 1; st2 >>= 1)
@@ -337,6 +365,21 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   // converted 16-byte chunk (8 values) of row r, logical chunk lc, into operand stage st
   auto put_chunks = [&](unsigned short* dst, int r, int lc, u32x4 w) __attribute__((always_inline)) {
     *reinterpret_cast<u32x4*>(dst + r * D + 8 * (lc ^ swz<SWZ>(r))) = w;
+  };
+  // 4 codes -> 4 fp16 values code * s (s: the row's scale times its normaliser, rounded to fp16).
+  // The codes become exact fp16 as in i8x4_to_f16x4 (byte + 128 in the low mantissa bits of 1024,
+  // minus 1152), written out here: routed through that helper's u32x2 result, the packed
+  // multiply that follows lost its second half in hipcc (ROCm 7.2) -- both words came out equal.
+  auto scaled4 = [&](unsigned codes, f16x2 s2v) __attribute__((always_inline)) {
+    const unsigned u = codes ^ 0x80808080u;
+    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const f16x2 lo = (__builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u)) + bias) * s2v;
+    const f16x2 hi = (__builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u)) + bias) * s2v;
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  };
+  auto half2_of = [&](float sv) __attribute__((always_inline)) {
+    const _Float16 hv = (_Float16)sv;
+    return f16x2{hv, hv};
   };
 
   if constexpr (DMA) {
@@ -386,7 +429,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
       else wait_vmcnt<SPW>();
     };
     // staging stage s8 -> operand stage st: thread tid converts chunk tid + 64 NW u of the 2 BN D / 16
-    // chunks (K chunks first); threads 0 .. 2 BN - 1 move the scales (v_s times 2^-E)
+    // chunks (K chunks first), scaling each row by its scale times the block normaliser
     auto convert = [&](auto s8, auto stage) __attribute__((always_inline)) {
       constexpr int NCH8 = 2 * BN * D / 16;
 #pragma unroll
@@ -396,22 +439,12 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
         const int cm = is_v ? ci - NCH8 / 2 : ci;
         const u32x4 w = *reinterpret_cast<const u32x4*>(&lds_q8[static_cast<int>(s8)][16 * ci]);
         const int r = (16 * cm) / D, lc = 2 * ((16 * cm) % D / 16);
-        if (is_v) {
-          const u32x2 x0 = i8x4_to_f16x4(w[0]), x1 = i8x4_to_f16x4(w[1]);
-          const u32x2 x2 = i8x4_to_f16x4(w[2]), x3 = i8x4_to_f16x4(w[3]);
-          put_chunks(lds_v[static_cast<int>(stage)], r, lc, u32x4{x0[0], x0[1], x1[0], x1[1]});
-          put_chunks(lds_v[static_cast<int>(stage)], r, lc + 1, u32x4{x2[0], x2[1], x3[0], x3[1]});
-        } else {
-          const u32x2 x0 = i8x4_to_bf16x4(w[0]), x1 = i8x4_to_bf16x4(w[1]);
-          const u32x2 x2 = i8x4_to_bf16x4(w[2]), x3 = i8x4_to_bf16x4(w[3]);
-          put_chunks(lds_k[static_cast<int>(stage)], r, lc, u32x4{x0[0], x0[1], x1[0], x1[1]});
-          put_chunks(lds_k[static_cast<int>(stage)], r, lc + 1, u32x4{x2[0], x2[1], x3[0], x3[1]});
-        }
-      }
-      if (tid < 2 * BN) {
-        const float sv = lds_s8[static_cast<int>(s8)][tid];
-        if (tid < BN) lds_ks[static_cast<int>(stage)][tid] = sv;
-        else lds_vs[static_cast<int>(stage)][tid - BN] = sv * vs_norm;
+        const f16x2 sr = half2_of(lds_s8[static_cast<int>(s8)][(is_v ? BN : 0) + r] * (is_v ? vs_norm : ks_norm));
+        const u32x2 x0 = scaled4(w[0], sr), x1 = scaled4(w[1], sr);
+        const u32x2 x2 = scaled4(w[2], sr), x3 = scaled4(w[3], sr);
+        unsigned short* dst = is_v ? lds_v[static_cast<int>(stage)] : lds_k[static_cast<int>(stage)];
+        put_chunks(dst, r, lc, u32x4{x0[0], x0[1], x1[0], x1[1]});
+        put_chunks(dst, r, lc + 1, u32x4{x2[0], x2[1], x3[0], x3[1]});
       }
     };
     // iteration t: compute tile t, convert tile t + 1, copy tile t + 3, wait for tile t + 2, barrier
@@ -455,18 +488,17 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     // ---- staging through registers: tile rows k0 .. k0 + 63 are read as 8-byte chunks of codes
     // with buffer loads (a scalar resource per tile, based at row k0 and ending at the head's last
     // key, plus a constant per-lane offset; rows past the end read as zero and are masked in the
-    // softmax), double-buffered in registers, converted exactly (K -> bf16, V -> fp16) and written
-    // to LDS at row r, physical chunk lc ^ swz(r).  Waves 0 and 1 also fetch the tile's scales.
+    // softmax), double-buffered in registers with the scales of their rows, converted (K~, V~)
+    // and written to LDS at row r, physical chunk lc ^ swz(r).
     u32x2 kreg[CH], vreg[CH];
-    int soff[CH];
+    float ksr[CH], vsr[CH];
+    int soff[CH], srow[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int idx = min(tid + 64 * NW * u, BN * NC - 1);
       soff[u] = (idx / NC) * D + 8 * (idx % NC);
+      srow[u] = idx / NC;
     }
-    const float* scale_src = (wave & 1) ? a.v_scale : a.k_scale;
-    const float scale_mul = (wave & 1) ? vs_norm : 1.f;
-    float sreg = 0.f;
     auto load_tile = [&](int t) __attribute__((always_inline)) {
       const int k0 = (t_lo + t) * BN;
       const int64_t rem = (int64_t)(a.s_k - k0) * D;
@@ -479,10 +511,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
       for (int u = 0; u < CH; ++u) {
         kreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, soff[u], 0, 0));
         vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, soff[u], 0, 0));
+        const int64_t key = kv_base + min(k0 + srow[u], last_key);
+        ksr[u] = a.k_scale[key];
+        vsr[u] = a.v_scale[key];
       }
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(scale_src + kv_base + k0), 0, (a.s_k - k0) * 4, kBufferFlags);
-      sreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0)) * scale_mul;
     };
     auto store_tile = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -490,15 +522,12 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
         const int idx = tid + 64 * NW * u;
         if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
           const int r = idx / NC, lc = idx % NC;
-          const u32x2 k0v = i8x4_to_bf16x4(kreg[u][0]), k1v = i8x4_to_bf16x4(kreg[u][1]);
-          const u32x2 v0v = i8x4_to_f16x4(vreg[u][0]), v1v = i8x4_to_f16x4(vreg[u][1]);
+          const f16x2 sk = half2_of(ksr[u] * ks_norm), sv = half2_of(vsr[u] * vs_norm);
+          const u32x2 k0v = scaled4(kreg[u][0], sk), k1v = scaled4(kreg[u][1], sk);
+          const u32x2 v0v = scaled4(vreg[u][0], sv), v1v = scaled4(vreg[u][1], sv);
           put_chunks(lds_k[st], r, lc, u32x4{k0v[0], k0v[1], k1v[0], k1v[1]});
           put_chunks(lds_v[st], r, lc, u32x4{v0v[0], v0v[1], v1v[0], v1v[1]});
         }
-      }
-      if (tid < 2 * BN) {
-        if (tid < BN) lds_ks[st][tid] = sreg;
-        else lds_vs[st][tid - BN] = sreg;
       }
     };
     // the global loads of tile t+1 are in flight while tile t is computed
@@ -516,7 +545,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     }
   }
 
-  // ---- finalize: O / l x 2^E, epilogue, store; LSE = sigma m + ln l
+  // ---- finalize: O / l x 2^Ev, epilogue, store; LSE = sigma m + ln l (m in units of S~)
   const float l_tot = add_xor32(l_run);
   float inv = l_tot > 0.f ? __fdiv_rn(1.0f, l_tot) : 0.f;
   inv *= vs_unnorm;
@@ -543,7 +572,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = w;
         }
       }
-    if (a.lse && h == 0) a.lse[row] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : neg_inf();
+    if (a.lse && h == 0) a.lse[row] = l_tot > 0.f ? m_run * ldexpf(a.scale, es) + logf(l_tot) : neg_inf();
   }
 }
 

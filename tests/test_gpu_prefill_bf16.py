@@ -146,6 +146,49 @@ def test_int8_kv_small_and_large_value_scales():
     check_close(o[1] / 3e4, ref[1] / 3e4, TOL_BF16, "large V (relative)")
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_int8_kv_query_and_key_magnitudes(d):
+    """The int8 path computes Q K^T in fp16 with a power-of-two scale per query row and per block
+    of key scales.  Key scales of 1e-4 and 3e4 (offset by the queries, so that the scores stay of
+    unit size), rows of magnitude 1/2, 1 and 2, and the whole of Q multiplied by 2^20 or 2^-20
+    with the softmax scale divided by the same power: all give the oracle's unscaled result."""
+    import math
+    torch = torch_gpu()
+    say(f"int8 magnitudes d={d}")
+    s = 333
+    q, k, v = rng_normal(79 + d, (4, s, d), (2, s, d), (2, s, d))
+    q = q * (np.float32(2.0) ** ((np.arange(s) % 3) - 1).astype(np.float32))[None, :, None]
+    k[0] *= np.float32(1e-4)
+    k[1] *= np.float32(3e4)
+    q[:2] *= np.float32(1e4)      # query heads 0, 1 read KV head 0 (group of 2)
+    q[2:] /= np.float32(3e4)      # query heads 2, 3 read KV head 1
+    q = round_bf16(q)
+    sigma = 1.0 / math.sqrt(d)
+    for qf in (1.0, 2.0 ** 20, 2.0 ** -20):
+        qq = (q * np.float32(qf)).astype(np.float32)   # exact: a power of two times bf16 values
+        for causal in (True, False):
+            out, (kq, ks, vq, vs) = _int8(qq, k, v, causal=causal, scale=sigma / qf, out_dtype=torch.float32)
+            ref, _ = oracle.attention(q, kq, vq, causal=causal, k_scale=ks, v_scale=vs)
+            check_close(to_np(out), ref, TOL_BF16, f"d={d} q x {qf:g} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_kv_masked_keys_with_large_scales(d):
+    """Keys that a block loads but masks (the window's lower edge) may have far larger scales than
+    the visible ones: the block's fp16 normalisers cover every loaded key, so nothing overflows
+    into the masked zeros of P (0 * inf), and the visible keys keep the oracle's result."""
+    torch = torch_gpu()
+    q, k, v = rng_normal(88 + d, (2, 600, d), (2, 600, d), (2, 600, d))
+    q = round_bf16(q)
+    v[:, 192:247] *= np.float32(1e5)   # loaded by the second block of 256 rows, visible to none of them
+    k[:, 192:247] *= np.float32(1e3)
+    out, (kq, ks, vq, vs) = _int8(q, k, v, causal=True, window=10, out_dtype=torch.float32)
+    o = to_np(out)
+    assert np.all(np.isfinite(o))
+    ref, _ = oracle.attention(q, kq, vq, causal=True, window=10, k_scale=ks, v_scale=vs, rows=range(256, 600))
+    check_close(o[:, 256:], ref[:, 256:], TOL_BF16, "rows of the second and third blocks")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_tile_and_pair_boundaries(d):
     """Key lengths around the 64-key tile and the two-tile copy / barrier grouping (odd and even
