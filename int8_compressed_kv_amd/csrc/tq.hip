@@ -16,6 +16,7 @@
 // cell masses and first moments of the Beta(d/2, d/2) law integrated by Gauss-Legendre
 // quadrature.
 #include <cmath>
+#include <cstring>
 #include <vector>
 
 #include "device_common.hpp"
@@ -23,9 +24,10 @@
 namespace fa {
 namespace {
 
-// A segment of SEG = d/16 lanes owns a vector, 16 values per lane: NCH chunks of CE values
-// (16 bytes each), chunk j of lane sl being chunk sl + SEG j of the vector, so each 16-byte load
-// of a segment is one contiguous run.  Channel c = CE (sl + SEG j) + e: the Hadamard stages over
+// A segment of SEG = d/16 lanes owns a vector, 16 values per lane: lane sl holds channels
+// 16 sl .. 16 sl + 15 (NCH chunks of CE values, 16 bytes each), so its codes are one contiguous
+// 8- or 4-byte word and its loads and stores contiguous runs.  Channel c = 16 sl + CE j + e: the
+// Hadamard stages over
 // the bits of e and j stay inside the lane, the stages over the bits of sl cross lanes.
 template <int CE>
 struct Lay {
@@ -60,7 +62,7 @@ __device__ __forceinline__ float cross_sum(float a) {
 }
 
 // in-place Walsh-Hadamard (Sylvester order) over the d = 16 SEG values of a segment;
-// v[CE j + e] is channel CE (sl + SEG j) + e
+// v[CE j + e] is channel 16 sl + CE j + e
 template <int CE, int SEG>
 __device__ __forceinline__ void hadamard16(float (&v)[16], int sl) {
   constexpr int NCH = Lay<CE>::NCH;
@@ -100,7 +102,7 @@ __device__ __forceinline__ float segment_sum(float a) {
 template <int CE, int SEG>
 __device__ __forceinline__ void channel_factors(float (&f)[16], const int8_t* signs, int sl, float scale) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) f[i] = signs[CE * (sl + SEG * (i / CE)) + i % CE] < 0 ? -scale : scale;
+  for (int i = 0; i < 16; ++i) f[i] = signs[16 * sl + i] < 0 ? -scale : scale;
 }
 
 // code = the number of thresholds <= u, for an antisymmetric codebook (thresholds t, with
@@ -129,25 +131,44 @@ __device__ __forceinline__ unsigned tq_code(float u, const float (&tp)[7]) {
   return (unsigned)((cnt ^ m) + H);
 }
 
+// The same 4-bit count by table: the float bits of x (clamped to [2^-7, 2)) name one of 64
+// buckets, eight per binade (bits 20..25: the exponent's low three bits and the top three
+// mantissa bits).  Entry b holds the positive threshold inside bucket b (its bits, or all ones if
+// none) and the number of positive thresholds below the bucket, so the count at x is
+// base + (x >= thr), with x compared unclamped.  Valid when no bucket holds two thresholds and the
+// smallest is at least 2^-7 (checked on the host; the search above serves other codebooks).
+constexpr unsigned kTabLo = 0x3C000000u;   // 2^-7
+constexpr unsigned kTabHi = 0x3FFFFFFFu;   // the float below 2
+__host__ __device__ inline unsigned tab_bucket_lo(unsigned b) { return ((120u + (b >> 3)) << 23) | ((b & 7u) << 20); }
+
+__device__ __forceinline__ unsigned tq_code4_tab(float u, const u32x2* tab) {
+  const unsigned ub = __float_as_uint(u);
+  const unsigned m = (unsigned)((int)ub >> 31);
+  const unsigned xb = (ub & 0x7fffffffu) + m;   // |u|, or the float just below it when u < 0
+  const unsigned cb = min(max(xb, kTabLo), kTabHi);
+  const u32x2 e = tab[(cb >> 20) & 63u];
+  const unsigned cnt = e[1] + (xb >= e[0] ? 1u : 0u);
+  return (cnt ^ m) + 8u;
+}
+
 // Row groups (RPW rows, one per segment) a wave takes in turn; the channel factors are set up
 // once per wave.
 constexpr int kTqIter = 4;
 
-// The NCH 16-byte chunks of row r a lane holds (chunk j = chunk sl + SEG j of the row).
+// The NCH 16-byte chunks of row r a lane holds (its 16 NCH contiguous bytes).
 template <int ROW_BYTES, int SEG, int NCH>
 __device__ __forceinline__ void load_chunks(u32x4 (&w)[NCH], const void* x, int64_t r, int sl) {
-  const char* p = static_cast<const char*>(x) + r * ROW_BYTES + 16 * sl;
+  const char* p = static_cast<const char*>(x) + r * ROW_BYTES + 16 * NCH * sl;
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) w[j] = *reinterpret_cast<const u32x4*>(p + 16 * SEG * j);
+  for (int j = 0; j < NCH; ++j) w[j] = *reinterpret_cast<const u32x4*>(p + 16 * j);
 }
 
-template <int D, bool BF16_IN, int BITS>
+template <int D, bool BF16_IN, int BITS, bool TABLE>
 __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
   constexpr int CE = BF16_IN ? 8 : 4;        // values per 16-byte chunk
   constexpr int NCH = 16 / CE;
   constexpr int SEG = D / 16;                // lanes per vector
   constexpr int RPW = 64 / SEG;
-  constexpr int CB = CE * BITS / 8;          // packed bytes per chunk
   constexpr int ROW_BYTES = D * (BF16_IN ? 2 : 4);
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
@@ -156,6 +177,21 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
   float tp[7];
 #pragma unroll
   for (int k = 0; k < 7; ++k) tp[k] = a.thr[(1 << (BITS - 1)) + (k < (1 << (BITS - 1)) - 1 ? k : 0)];
+  __shared__ u32x2 tab[TABLE ? 64 : 1];
+  if constexpr (TABLE) {
+    if (threadIdx.x < 64) {
+      const unsigned lo = tab_bucket_lo(threadIdx.x), hi = lo + (1u << 20);
+      unsigned base = 0, thr = 0xffffffffu;
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        const unsigned tb = __float_as_uint(tp[k]);
+        base += tb < lo ? 1u : 0u;
+        thr = (tb >= lo && tb < hi) ? tb : thr;
+      }
+      tab[threadIdx.x] = u32x2{thr, base};
+    }
+    __syncthreads();
+  }
   const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
   // every lane takes part in the butterflies: rows past the end repeat the last row
   u32x4 cur[NCH], nxt[NCH];
@@ -194,18 +230,17 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
     const float ny = __fsqrt_rn(segment_sum<SEG>(yy));
     const float inv = ny > 0.f ? __fdiv_rn(1.0f, ny) : 0.f;
     if (row < a.n) {
+      // the lane's 16 codes, channel 16 sl + i at bit BITS i of a little-endian word
+      unsigned packed[BITS / 2] = {};
+      // fma with +0 rounds like the product and turns a -0 product into +0
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        unsigned packed = 0;
-        // fma with +0 rounds like the product and turns a -0 product into +0
-#pragma unroll
-        for (int e = 0; e < CE; ++e)
-          packed |= tq_code<BITS>(__builtin_fmaf(v[CE * j + e], inv, 0.0f), tp) << (BITS * e);
-        uint8_t* dst = a.codes + row * (D * BITS / 8) + (sl + SEG * j) * CB;
-        if constexpr (CB == 4) *reinterpret_cast<unsigned*>(dst) = packed;
-        else if constexpr (CB == 2) *reinterpret_cast<unsigned short*>(dst) = (unsigned short)packed;
-        else *dst = (uint8_t)packed;
-      }
+      for (int i = 0; i < 16; ++i)
+        packed[(BITS * i) / 32] |= (TABLE ? tq_code4_tab(__builtin_fmaf(v[i], inv, 0.0f), tab)
+                                          : tq_code<BITS>(__builtin_fmaf(v[i], inv, 0.0f), tp))
+                                   << ((BITS * i) % 32);
+      uint8_t* dst = a.codes + row * (D * BITS / 8) + sl * (2 * BITS);
+      if constexpr (BITS == 4) *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+      else *reinterpret_cast<unsigned*>(dst) = packed[0];
       if (sl == 0) a.norms[row] = n;
     }
 #pragma unroll
@@ -216,26 +251,29 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
 template <int D, bool BF16_OUT, int BITS>
 __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   constexpr int CE = 4;                       // fp32 values per chunk of the layout
-  constexpr int NCH = 4;
   constexpr int SEG = D / 16;
   constexpr int RPW = 64 / SEG;
-  constexpr int CB = CE * BITS / 8;
+  constexpr int NW = BITS / 2;                // 32-bit words of a lane's 16 codes
   __shared__ float cb[16];
   if (threadIdx.x < 16) cb[threadIdx.x] = a.cb[threadIdx.x];
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
   const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
-  // all row groups' codes and norms are loaded up front (rows past the end repeat the last row)
-  unsigned pk[kTqIter][NCH];
+  // all row groups' codes (the lane's contiguous 16) and norms are loaded up front (rows past the
+  // end repeat the last row)
+  unsigned pk[kTqIter][NW];
   float nn[kTqIter];
 #pragma unroll
   for (int it = 0; it < kTqIter; ++it) {
     const int64_t r = min((g0 + it) * RPW + lane / SEG, a.n - 1);
     nn[it] = a.norms[r];
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const uint8_t* src = a.codes + r * (D * BITS / 8) + (sl + SEG * j) * CB;
-      pk[it][j] = CB == 2 ? *reinterpret_cast<const unsigned short*>(src) : *src;
+    const uint8_t* src = a.codes + r * (D * BITS / 8) + sl * (2 * BITS);
+    if constexpr (NW == 2) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+      pk[it][0] = w[0];
+      pk[it][NW - 1] = w[1];
+    } else {
+      pk[it][0] = *reinterpret_cast<const unsigned*>(src);
     }
   }
   float f[16];
@@ -246,30 +284,44 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
     if ((g0 + it) * RPW >= a.n) break;
     const int64_t row = (g0 + it) * RPW + lane / SEG;
     float v[16];
+    // rounded on its own: an fma with the first butterfly's add would round differently
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      // rounded on its own: an fma with the first butterfly's add would round differently
-#pragma unroll
-      for (int e = 0; e < CE; ++e) v[CE * j + e] = mul_rn(nn[it], cb[(pk[it][j] >> (BITS * e)) & ((1u << BITS) - 1)]);
-    }
+    for (int i = 0; i < 16; ++i)
+      v[i] = mul_rn(nn[it], cb[(pk[it][(BITS * i) / 32] >> ((BITS * i) % 32)) & ((1u << BITS) - 1)]);
     hadamard16<CE, SEG>(v, sl);
     if (row < a.n) {
+      float y[16];
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int ch = sl + SEG * j;
-        float y[4];
+      for (int i = 0; i < 16; ++i) y[i] = v[i] * f[i];
+      if constexpr (BF16_OUT) {
+        unsigned short* dst = static_cast<unsigned short*>(a.out) + row * D + 16 * sl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = v[CE * j + e] * f[CE * j + e];
-        if constexpr (BF16_OUT) {
-          const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + CE * ch) = w;
-        } else {
-          const f32x4 w = {y[0], y[1], y[2], y[3]};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + CE * ch) = w;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4 w = {pack_bf16x2(y[8 * h2], y[8 * h2 + 1]), pack_bf16x2(y[8 * h2 + 2], y[8 * h2 + 3]),
+                           pack_bf16x2(y[8 * h2 + 4], y[8 * h2 + 5]), pack_bf16x2(y[8 * h2 + 6], y[8 * h2 + 7])};
+          *reinterpret_cast<u32x4*>(dst + 8 * h2) = w;
         }
+      } else {
+        float* dst = static_cast<float*>(a.out) + row * D + 16 * sl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(dst + 4 * j) = f32x4{y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]};
       }
     }
   }
+}
+
+// the table decision applies (4 bits; positive thresholds a.thr[8 ..] in distinct buckets, the
+// smallest at least 2^-7, the largest below 2)
+inline bool tq_table_ok(const TqArgs& a) {
+  unsigned prev = 0;
+  for (int k = 0; k < 7; ++k) {
+    unsigned tb;
+    std::memcpy(&tb, &a.thr[8 + k], 4);
+    if (tb < kTabLo || tb > kTabHi) return false;
+    if (k > 0 && (tb >> 20) == (prev >> 20)) return false;
+    prev = tb;
+  }
+  return true;
 }
 
 template <int D, int BITS>
@@ -277,9 +329,16 @@ hipError_t launch_encode_d(const TqArgs& a, bool bf16, hipStream_t st, const cha
   const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqIter;
   const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (bf16) hipLaunchKernelGGL((tq_encode_kernel<D, true, BITS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((tq_encode_kernel<D, false, BITS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  *name = "tq_encode";
+  const dim3 grid((unsigned)blocks), block(256);
+  if (BITS == 4 && tq_table_ok(a)) {
+    if (bf16) hipLaunchKernelGGL((tq_encode_kernel<D, true, BITS, BITS == 4>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((tq_encode_kernel<D, false, BITS, BITS == 4>), grid, block, 0, st, a);
+    *name = "tq_encode";
+  } else {
+    if (bf16) hipLaunchKernelGGL((tq_encode_kernel<D, true, BITS, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((tq_encode_kernel<D, false, BITS, false>), grid, block, 0, st, a);
+    *name = BITS == 4 ? "tq_encode_search" : "tq_encode";
+  }
   return hipGetLastError();
 }
 

@@ -56,6 +56,36 @@ def test_encode_matches_oracle_up_to_threshold_ties(d, bits, xdt):
                 "norms (relative)")
 
 
+@pytest.mark.parametrize("which", ["close", "tiny"])
+def test_encode_with_codebooks_outside_the_decision_table(which):
+    """4-bit encode decides through a table of float-bit buckets when the codebook fits it and by a
+    search otherwise; antisymmetric codebooks with two thresholds in one bucket ("close") or a
+    threshold below 2^-7 ("tiny") take the search and still match the oracle's codes."""
+    import int8_compressed_kv_amd as fa
+    torch = torch_gpu()
+    d = 128
+    pos = {"close": [0.01, 0.03, 0.05, 0.0504, 0.0508, 0.1, 0.2, 0.3],
+           "tiny": [0.001, 0.003, 0.01, 0.03, 0.06, 0.1, 0.2, 0.3]}[which]
+    cb = np.array([-x for x in pos[::-1]] + pos, np.float32)
+    x = rng_normal(1500, (3000, d))[0]
+    s = random_signs(1501, d)
+    codes, norms = fa.tq_encode(to_dev(x, "f32"), torch.from_numpy(s).cuda(), 4, cb)
+    assert fa.last_kernel() == "tq_encode_search"
+    got = oracle.tq_unpack(to_np(codes), 4, d)
+    t = (np.float32(0.5) * (cb[1:] + cb[:-1])).astype(np.float64)   # the fp32 midpoints the library uses
+    want, _ = oracle.tq_encode(x, s, 4, codebook=(cb.astype(np.float64), t))
+    y = (x.astype(np.float64) * s) @ oracle.hadamard(d).T
+    u = y / np.linalg.norm(y, axis=-1, keepdims=True)
+    gap = np.min(np.abs(u[..., None] - t), axis=-1)
+    diff = got != want
+    say(f"  {which}: codes differing {int(diff.sum())} of {diff.size}")
+    assert np.all(gap[diff] < 2e-6)
+    assert diff.sum() <= 1e-4 * diff.size + 2
+    # the Beta codebook takes the table
+    fa.tq_encode(to_dev(x, "f32"), torch.from_numpy(s).cuda(), 4, fa.tq_codebook(d, 4))
+    assert fa.last_kernel() == "tq_encode"
+
+
 @pytest.mark.parametrize("d,bits", [(64, 2), (128, 4), (256, 4), (32, 2)])
 def test_decode_matches_oracle_on_the_same_codes(d, bits):
     import int8_compressed_kv_amd as fa
