@@ -151,9 +151,11 @@ __device__ __forceinline__ unsigned tq_code4_tab(float u, const u32x2* tab) {
   return (cnt ^ m) + 8u;
 }
 
-// Row groups (RPW rows, one per segment) a wave takes in turn; the channel factors are set up
-// once per wave.
-constexpr int kTqIter = 4;
+// Row groups (RPW rows, one per segment) a wave takes in turn, the channel factors set up once
+// per wave: one for encode, four for decode (interleaved timings at the C4 K cache: encode 0.50 ms
+// with one group, 0.52-0.53 with 2, 4 or 8; decode 0.32 ms with four, 0.34 with 1, 2 or 8).
+constexpr int kTqEncIter = 1;
+constexpr int kTqDecIter = 4;
 
 // The NCH 16-byte chunks of row r a lane holds (its 16 NCH contiguous bytes).
 template <int ROW_BYTES, int SEG, int NCH>
@@ -192,16 +194,16 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
     }
     __syncthreads();
   }
-  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqEncIter;
   // every lane takes part in the butterflies: rows past the end repeat the last row
   u32x4 cur[NCH], nxt[NCH];
   load_chunks<ROW_BYTES, SEG, NCH>(cur, a.x, min(g0 * RPW + lane / SEG, a.n - 1), sl);
 #pragma unroll
-  for (int it = 0; it < kTqIter; ++it) {
+  for (int it = 0; it < kTqEncIter; ++it) {
     if ((g0 + it) * RPW >= a.n) break;
     const int64_t row = (g0 + it) * RPW + lane / SEG;
     // the next row group's loads go out before this one's arithmetic
-    if (it + 1 < kTqIter && (g0 + it + 1) * RPW < a.n)
+    if (it + 1 < kTqEncIter && (g0 + it + 1) * RPW < a.n)
       load_chunks<ROW_BYTES, SEG, NCH>(nxt, a.x, min(row + RPW, a.n - 1), sl);
     float v[16];
 #pragma unroll
@@ -243,8 +245,10 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
       else *reinterpret_cast<unsigned*>(dst) = packed[0];
       if (sl == 0) a.norms[row] = n;
     }
+    if (it + 1 < kTqEncIter) {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
+      for (int j = 0; j < NCH; ++j) cur[j] = nxt[j];
+    }
   }
 }
 
@@ -258,13 +262,13 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   if (threadIdx.x < 16) cb[threadIdx.x] = a.cb[threadIdx.x];
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
-  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqIter;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqDecIter;
   // all row groups' codes (the lane's contiguous 16) and norms are loaded up front (rows past the
   // end repeat the last row)
-  unsigned pk[kTqIter][NW];
-  float nn[kTqIter];
+  unsigned pk[kTqDecIter][NW];
+  float nn[kTqDecIter];
 #pragma unroll
-  for (int it = 0; it < kTqIter; ++it) {
+  for (int it = 0; it < kTqDecIter; ++it) {
     const int64_t r = min((g0 + it) * RPW + lane / SEG, a.n - 1);
     nn[it] = a.norms[r];
     const uint8_t* src = a.codes + r * (D * BITS / 8) + sl * (2 * BITS);
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   channel_factors<CE, SEG>(f, a.signs, sl, a.inv_sqrt_d);
   __syncthreads();
 #pragma unroll
-  for (int it = 0; it < kTqIter; ++it) {
+  for (int it = 0; it < kTqDecIter; ++it) {
     if ((g0 + it) * RPW >= a.n) break;
     const int64_t row = (g0 + it) * RPW + lane / SEG;
     float v[16];
@@ -326,7 +330,7 @@ inline bool tq_table_ok(const TqArgs& a) {
 
 template <int D, int BITS>
 hipError_t launch_encode_d(const TqArgs& a, bool bf16, hipStream_t st, const char** name) {
-  const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqIter;
+  const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqEncIter;
   const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(256);
@@ -344,7 +348,7 @@ hipError_t launch_encode_d(const TqArgs& a, bool bf16, hipStream_t st, const cha
 
 template <int D, int BITS>
 hipError_t launch_decode_d(const TqArgs& a, bool bf16_out, hipStream_t st, const char** name) {
-  const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqIter;
+  const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqDecIter;
   const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (bf16_out) hipLaunchKernelGGL((tq_decode_kernel<D, true, BITS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
