@@ -386,9 +386,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     // Per tile: wave w copies K/V segments SPW w .. SPW w + SPW - 1 (segment gs < SEGS is K
     // segment gs, else V segment gs - SEGS; lane l of a segment brings the 16 codes at byte
     // 1024 seg + 16 l of the row-major tile), wave 0 the 64 k scales and wave 1 the 64 v scales.
-    // Tile t + 3's copies are issued after tile t is computed and converted-ahead, so after the
-    // barrier that ended the conversion of tile t - 1 (the last reader of that staging stage),
-    // and waited for at the end of iteration t + 2.
+    // Tile t + 3's copies are issued in iteration t, after the barrier that ended the conversion
+    // of tile t - 1 (the last reader of that staging stage, in iteration t - 2); each wave waits
+    // for its own copies of tile t + 3 at the end of iteration t + 1, before the barrier that
+    // precedes their conversion in iteration t + 2.
     const unsigned q8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int8_t*)&lds_q8[0][0];
     const unsigned s8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)&lds_s8[0][0];
     int crow[SPW], ccol[SPW];
