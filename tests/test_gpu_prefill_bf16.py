@@ -204,3 +204,21 @@ def test_tile_and_pair_boundaries(d):
             out = _bf16(q, k, v, causal=causal, window=window, out_dtype=torch.float32)
             ref, _ = oracle.attention(q, k, v, causal=causal, window=window)
             check_close(to_np(out), ref, TOL_BF16, f"s_q={s_q} s_k={s_k} causal={causal} window={window}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_kv_tile_and_pipeline_boundaries(d):
+    """The int8 cache's staging pipeline (copies of tile t + 3 in flight, conversion one tile
+    ahead) at 1 to 5 tiles, full and partial last tiles, causal, windowed and bottom-right aligned
+    shapes, against the dequantized oracle."""
+    torch = torch_gpu()
+    say(f"int8 tile/pipeline boundaries d={d}")
+    cases = [(1, 1), (63, 63), (64, 64), (65, 65), (128, 128), (129, 129), (191, 191), (192, 192),
+             (257, 257), (70, 200), (5, 321)]
+    for i, (s_q, s_k) in enumerate(cases):
+        q, k, v = rng_normal(1900 + 7 * d + i, (4, s_q, d), (2, s_k, d), (2, s_k, d))
+        q = round_bf16(q)
+        for causal, window in [(True, 0), (False, 0), (True, 65)]:
+            out, (kq, ks, vq, vs) = _int8(q, k, v, causal=causal, window=window, out_dtype=torch.float32)
+            ref, _ = oracle.attention(q, kq, vq, causal=causal, window=window, k_scale=ks, v_scale=vs)
+            check_close(to_np(out), ref, TOL_BF16, f"s_q={s_q} s_k={s_k} causal={causal} window={window}")
