@@ -17,7 +17,8 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
          that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to HBM bytes
 
 One JSON line on stdout; progress on stderr.  `--gpus N` with N > 1 exits: this path runs on one
-GPU (a multi-GPU run would shard KV heads).
+GPU (a multi-GPU run would give each GPU a share of the KV heads, with their query heads, and
+run the same kernels on it; no data moves between GPUs for the prefill or the decode).
 """
 from __future__ import annotations
 
