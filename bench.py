@@ -94,6 +94,43 @@ def blas_threads():
         return 1
 
 
+def shader_clock_under_load(torch, fn, seconds=2.0):
+    """Median shader clock (MHz) that `rocm-smi --showclocks` reports while `fn` runs back to back
+    for about `seconds` (untimed; the caller's timed steps are already done), or None when the tool
+    is missing or prints no clock."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            m = re.search(r"sclk clock level:\s*\S+:?\s*\((\d+)\s*Mhz\)", txt, re.IGNORECASE)
+            if m:
+                samples.append(int(m.group(1)))
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.time()
+    fn()
+    torch.cuda.synchronize()
+    th.start()
+    while time.time() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    return float(np.median(samples)) if samples else None
+
+
 class Timer:
     """HIP events around each call on the current stream; returns per-call milliseconds."""
 
@@ -172,6 +209,11 @@ def main():
                          "flop_per_launch": flops, "tflops": flops / avg / 1e9,
                          "frac_of_peak": flops / avg / 1e9 / PEAK_BF16_TFLOPS}
             log(f"[bench] {name}: {avg:.3f} ms  {res[name]['tflops']:.1f} TFLOP/s")
+            if name == "c5":
+                mhz = shader_clock_under_load(torch, fn)
+                res[name]["clock_mhz"] = mhz
+                if mhz:
+                    log(f"[bench] c5: shader clock under this load {mhz:.0f} MHz (rocm-smi)")
             if name == "c5" and not args.no_cpu:
                 cpu["c5"] = prefill_cpu_baseline(q, k, v, out, w, args.cpu_seconds)
         del qd, kd, vd, out, q, k, v
@@ -327,6 +369,11 @@ def main():
                             "unit": "TFLOP/s", "frac": round(r["frac_of_peak"], 4),
                             "traffic": traffic_for("c5"),
                             "kernel": r["kernel"], "flop_per_launch": r["flop_per_launch"]}
+        # the same fraction against the peak at the shader clock measured under this load
+        mhz = r.get("clock_mhz")
+        line["roofline"]["clock_mhz"] = mhz
+        line["roofline"]["frac_at_clock"] = (round(r["tflops"] / (PEAK_BF16_TFLOPS * mhz / 2400.0), 4)
+                                             if mhz else None)
     if "c4" in res:
         r = res["c4"]
         line["decode"] = {"metric": "int8-KV decode GB/s", "value": round(r["gbs"], 1), "unit": "GB/s",
