@@ -180,7 +180,10 @@ int fa_tq_codebook(int32_t head_dim, int32_t bits, float* centroids);
  *              (i bits) mod 8 of byte (i bits) / 8.
  *   norms_out  device fp32 [n_tokens]: ||x||_2.
  * y = H (signs * x) (Sylvester Hadamard), u = y / ||y||, code_i = the number of midpoints
- * between consecutive centroids that are <= u_i.  Decisions are taken in fp32.
+ * between consecutive centroids that are <= u_i.  Decisions are taken in fp32; at 4 bits they go
+ * through a table of float-bit buckets when the codebook fits it (fa_last_kernel() "tq_encode",
+ * as for fa_tq_codebook's codebooks) and through a search otherwise ("tq_encode_search"), with
+ * the same result.
  * n_tokens == 0 is a no-op.
  */
 int fa_tq_encode(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_dim, int32_t bits,
