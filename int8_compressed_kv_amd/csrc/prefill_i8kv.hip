@@ -437,6 +437,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     // chunks (K chunks first), scaling each row by its scale times the block normaliser
     auto convert = [&](auto s8, auto stage) __attribute__((always_inline)) {
       constexpr int NCH8 = 2 * BN * D / 16;
+      __builtin_amdgcn_iglp_opt(0);   // the same interleave hint (1-2% on C3, both orders timed)
 #pragma unroll
       for (int u = 0; u < NCH8 / (64 * NW); ++u) {
         const int ci = tid + 64 * NW * u;
