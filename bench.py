@@ -7,6 +7,8 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   c5w    the same with a 4096-token sliding window
   c3     int8-KV causal prefill, bf16 Q, 4 x 32 heads, 4096 tokens, d 128, bf16 output
   c4     GQA split-KV decode over the int8 cache, 16 x 32 query / 8 KV heads, 32768 keys, d 128
+  c4g8   the same cache with a GQA group of 8 (16 x 64 query / 8 KV heads): one workgroup serves
+         all 8 query heads of a KV head, so the cache is still read once
   comp   per-token compression of the c4 K and V caches (fp32 -> int8 + fp32 scales)
   append decode-time cache write of the c4 shape: one new fp32 K and V token per KV head (128),
          quantized into the 32768-row int8 cache at device-held positions (latency-bound)
@@ -56,6 +58,7 @@ LEG_SOURCES = {
     "c5w": ("prefill_bf16.hip", "device_common.hpp", "kernel_args.hpp"),
     "c3": ("prefill_i8kv.hip", "device_common.hpp", "kernel_args.hpp"),
     "c4": ("decode.hip", "device_common.hpp", "kernel_args.hpp"),
+    "c4g8": ("decode.hip", "device_common.hpp", "kernel_args.hpp"),
     "comp": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
     "append": ("compress.hip", "device_common.hpp", "kernel_args.hpp"),
     "merge": ("merge.hip", "device_common.hpp", "kernel_args.hpp"),
@@ -161,7 +164,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="c5,c5w,c3,c4,comp,append,merge,tq")
+    ap.add_argument("--legs", default="c5,c5w,c3,c4,c4g8,comp,append,merge,tq")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
     args = ap.parse_args()
@@ -239,7 +242,7 @@ def main():
         del qd, kc, ks, vc, vs, out, q, k, v
 
     # ------------------------------------------------------------------ compress + decode c4
-    if legs & {"c4", "comp", "append", "tq"}:
+    if legs & {"c4", "c4g8", "comp", "append", "tq"}:
         w = WORKLOADS["c4"]
         log(f"[bench] generating {w.name}")
         q, k, v = draw_qkv(w)
@@ -322,6 +325,25 @@ def main():
             log(f"[bench] c4: {avg * 1e3:.1f} us  {res['c4']['gbs']:.0f} GB/s")
             if not args.no_cpu:
                 cpu["c4"] = decode_cpu_baseline(q, kc, ks, vc, vs, out, w, args.cpu_seconds)
+        if "c4g8" in legs:
+            # 8 query heads per KV head over the same cache: Q drawn from PCG64(48), bf16
+            g8 = 8
+            bh_q8 = w.bh_kv * g8
+            q8 = bf16_dev(np.random.Generator(np.random.PCG64(48)).standard_normal((bh_q8, 1, w.d), dtype=np.float32))
+            out8 = torch.empty((bh_q8, 1, w.d), dtype=torch.float32, device="cuda")
+            splits8 = fa.decode_num_splits(bh_q8, w.bh_kv, w.s_k, w.d)
+            ws8 = torch.empty(fa.decode_workspace_bytes(bh_q8, w.bh_kv, w.s_k, w.d, splits8), dtype=torch.uint8,
+                              device="cuda")
+            fn8 = lambda: fa.decode(q8, kc, vc, ks, vs, num_splits=splits8, out=out8, workspace=ws8)   # noqa: E731
+            log("[bench] timing decode with GQA group 8")
+            ms = timer.run(fn8, args.steps, args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = (2 * w.bh_kv * w.s_k * w.d + 2 * w.bh_kv * w.s_k * 4 + bh_q8 * w.d * 2 + bh_q8 * w.d * 4)
+            res["c4g8"] = {"workload": "decode_g8_b16_h64kv8_sk32768_d128", "ms": avg, "ms_min": float(np.min(ms)),
+                           "kernel": fa.last_kernel(), "num_splits": splits8, "bytes_per_launch": nbytes,
+                           "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] c4g8: {avg * 1e3:.1f} us  {res['c4g8']['gbs']:.0f} GB/s")
+            del q8, out8, ws8
         del qd, kc, vc, ks, vs, out, ws
 
     if "merge" in legs:

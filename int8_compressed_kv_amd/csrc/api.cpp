@@ -313,10 +313,10 @@ int fa_tq_decode(const uint8_t* codes, const float* norms, int64_t n_tokens, int
 }
 
 int32_t fa_decode_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim) {
-  (void)head_dim;
   if (bh_kv <= 0 || bh_q <= 0 || s_k <= 0) return 1;
   const int32_t group = bh_q / bh_kv;
-  const int32_t col_groups = (group + 3) / 4;   // decode workgroups per (split, KV head)
+  const int32_t hpw = fa::decode_heads_per_workgroup(group, head_dim);
+  const int32_t col_groups = (group + hpw - 1) / hpw;   // decode workgroups per (split, KV head)
   const int64_t units = (int64_t)bh_kv * col_groups;
   const int32_t tiles = (s_k + kDecodeTile - 1) / kDecodeTile;
   // one workgroup per CU (256), each split keeping at least 16 tiles (4 per wave)

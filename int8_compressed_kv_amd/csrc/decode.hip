@@ -3,13 +3,15 @@
 // dequantized inside q.k and p.v and never expanded in global memory; kernbench2 ADR-0060
 // commit: split decode whose partial running (m, l, O) states are reduced afterwards).
 //
-// Pass 1 (decode_partial_kernel), grid (splits, bh_kv, ceil(G/4)): a workgroup streams one
-// contiguous range of keys of one KV head for up to 4 query heads of its GQA group and leaves
-// one partial state (m, l, O unnormalised) per (query head, split) in the workspace.
+// Pass 1 (decode_partial_kernel), grid (splits, bh_kv, ceil(G/H)): a workgroup streams one
+// contiguous range of keys of one KV head for up to H query heads of its GQA group (H = 4, or
+// 8 as two MFMA column sets when G > 4 and head_dim <= 128) and leaves one partial state
+// (m, l, O unnormalised) per (query head, split) in the workspace.
 // Pass 2 (decode_merge_kernel): per query head, M = max m_s, L = sum l_s e^(m_s - M),
 // O = sum O_s e^(m_s - M) / L, then the epilogue and the store.
 //
-// HBM-bound.  Every K/V byte is read once for all query heads of its group.  Each wave streams
+// HBM-bound.  Every K/V byte is read once for all query heads of its group when G <= H (G <= 8
+// at head_dim <= 128, G <= 4 above; a larger group reads the cache ceil(G/H) times).  Each wave streams
 // its own tiles of 32 keys with plain 16-byte vector loads into two register tiles (the next
 // tile is in flight while the current one is computed): on gfx950 this sustains a higher read
 // rate than direct global -> LDS copies.  All cache reads, the per-key scales included, are
@@ -26,11 +28,14 @@
 //     (digit, head): 4 digits x 4 heads fill the 16 columns that a single decode row would
 //     otherwise leave empty.  The int32 products are exact; the digit columns are recombined
 //     in fp32 with two DPP row rotations, so every lane ends up with the same S.
-//   * O += P~ V with P~ = p * v_s.  B holds P~ as four unsigned 7-bit digits of P~ / 2^F
-//     (2^F above the largest P~ so far), one column per (digit, head).  A = V^T codes, read
-//     with transposing LDS reads (ds_read_b64_tr_b8) from the row-major tile.  The products
-//     accumulate exactly in the int32 MFMA accumulators across tiles and are moved to fp32
-//     only when the running max is raised or P~ outgrows 2^F (about 26 bits of P~ kept).
+//   * O += P~ V with P~ = p * v_s.  x = P~ / 2^F (2^F above every P~ since the last flush) is
+//     rounded to nearest at 28 fractional bits and split into four unsigned 7-bit digits, one
+//     MFMA column per (digit, head).  A = V^T codes, read with transposing LDS reads
+//     (ds_read_b64_tr_b8) from the row-major tile.  The products accumulate exactly in the
+//     int32 MFMA accumulators across tiles and are moved to fp32 when the running max is raised,
+//     when P~ outgrows 2^F, or after kFlushTiles tiles; F then restarts from the current tile.
+//     Each P~ thus carries an unbiased rounding error of at most 2^(F - 29), F set by the
+//     largest P~ of the tiles since the last flush under the same running max.
 //   * Key order: MFMA row r of row-block kb holds key (KT/4)(r/4) + 4 kb + r%4, so lane group
 //     g of the score accumulator owns keys (KT/4) g .. (KT/4) g + KT/4 - 1 -- exactly the keys
 //     the transposing read gives that lane group for the P~ V product.
@@ -38,6 +43,7 @@
 #include "device_common.hpp"
 
 namespace fa {
+
 namespace {
 
 constexpr float kLazyLog2 = 8.0f;
@@ -70,7 +76,7 @@ __device__ __forceinline__ int dswz(int r) {
   return ((r >> 1) ^ (r >> 4)) & (SP - 1);
 }
 
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeArgs a) {
   using C = DCfg<D>;
   constexpr int KT = C::KT, NC16 = C::NC16, SP = C::SP, VCH = C::VCH;
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   constexpr int KB = KT / 16;                   // 16-row blocks of S per tile
   constexpr int NKK = (D + 63) / 64;            // 64-deep k-steps of Q.K
   constexpr int NB = D / 16;                    // 16-row blocks of O^T
-  constexpr int HPW = 4;                        // query heads per workgroup
+  constexpr int HPW = 4 * NS;                   // query heads per workgroup (NS column sets of 4)
 
   __shared__ __attribute__((aligned(16))) unsigned char lds_slot[kWaves][C::SLOT];
   __shared__ float lds_m[kWaves][HPW];
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = lane & 15;        // MFMA column: digit t = n / 4, head-in-tile gq = n % 4
+  const int n = lane & 15;        // MFMA column: digit t = n / 4, head-in-set gq = n % 4
   const int hq = lane >> 4;       // lane group (k-slot group of A/B, row group of C)
   const int t_dig = n >> 2;
   const int gq = n & 3;
@@ -100,14 +106,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   const int64_t kv_base = (int64_t)kvh * a.s_k;
   const int head0 = kvh * a.group + zh;
 
-  // ---- Q digit B operands: column n = (t_dig, gq), k-slots 64 kk + 16 hq + i.  Each lane loads
-  // its 16 contiguous head-dim values per k-step; E (max|q| * 2^-E < 1/2) comes from a max over
-  // the lane's values and the other three lane groups (which hold the rest of the same head).
-  i32x4 qdig[NKK];
-  float s_comb;   // 2^(E - 7 (t + 1)) for this lane's digit column
-  {
-    const bool hv = gq < nh;
-    const int64_t qrow = (int64_t)(head0 + (hv ? gq : 0)) * D;
+  // ---- Q digit B operands: column set c, column n = (t_dig, gq) is head 4 c + gq; k-slots
+  // 64 kk + 16 hq + i.  Each lane loads its 16 contiguous head-dim values per k-step; E
+  // (max|q| * 2^-E < 1/2) comes from a max over the lane's values and the other three lane
+  // groups (which hold the rest of the same head).
+  i32x4 qdig[NS][NKK];
+  float s_comb[NS];   // 2^(E - 7 (t + 1)) for this lane's digit column
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    const bool hv = 4 * c + gq < nh;
+    const int64_t qrow = (int64_t)(head0 + (hv ? 4 * c + gq : 0)) * D;
     float qv[NKK][16];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
       (void)frexpf(mx, &E);   // mx = f * 2^E, f in [0.5, 1)
       E += 1;
     }
-    s_comb = ldexpf(1.f, E - 7 * (t_dig + 1));
+    s_comb[c] = ldexpf(1.f, E - 7 * (t_dig + 1));
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       unsigned w[4] = {0u, 0u, 0u, 0u};
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         const int dig = (int)(t_dig == 0 ? dd[0] : t_dig == 1 ? dd[1] : t_dig == 2 ? dd[2] : dd[3]);
         w[i / 4] |= ((unsigned)dig & 0xffu) << (8 * (i % 4));
       }
-      qdig[kk] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      qdig[c][kk] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
   }
 
@@ -227,31 +235,41 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   };
   unsigned char* slot = &lds_slot[wave][0];
 
-  // O = Of + Oi * 2^(F - 7 (t + 1)): exact int32 MFMA sums since the last flush (Oi) and the
-  // fp32 total before it (Of).  Oi is flushed when the running max is raised, when P~ outgrows
-  // 2^F, and every kFlushTiles tiles.
-  float Of[NB][4];
-  i32x4 Oi[NB];
+  // Per column set: O = Of + Oi * 2^(F - 7 (t + 1)), Oi the exact int32 MFMA sums of P~ V since
+  // the last flush and Of the fp32 total before it.  Oi is flushed when the running max is
+  // raised, when P~ outgrows 2^F, and every kFlushTiles tiles; after a flush the digit scale F
+  // restarts from the current tile's largest P~ (Oi is empty then), so it never stays high
+  // after a raise of the running max.
+  float Of[NS][NB][4];
+  i32x4 Oi[NS][NB];
+  float m_run[NS], l_run[NS], mc[NS];
+  int F[NS];                 // digit scale of Oi (per head column; equal on its 4 digit lanes)
+  int since_flush[NS];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    Oi[b] = i32x4{0, 0, 0, 0};
+  for (int c = 0; c < NS; ++c) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) Of[b][v] = 0.f;
+    for (int b = 0; b < NB; ++b) {
+      Oi[c][b] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Of[c][b][v] = 0.f;
+    }
+    m_run[c] = neg_inf();
+    l_run[c] = 0.f;
+    mc[c] = 0.f;
+    F[c] = -1000;
+    since_flush[c] = 0;
   }
-  float m_run = neg_inf(), l_run = 0.f, mc = 0.f;
-  int F = -1000;             // digit scale of Oi (per head column; equal on its 4 digit lanes)
-  int since_flush = 0;
   const float c2 = a.scale_log2;
   const float lazy_thr = kLazyLog2 / c2;
-  auto flush = [&]() {
-    const float sc = ldexpf(1.f, F - 7 * (t_dig + 1));
+  // Oi -> Of.  ldexp keeps the scaling exact (no overflow of a separately formed 2^x) for any F.
+  auto flush = [&](int c) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Of[b][v] = __builtin_fmaf((float)Oi[b][v], sc, Of[b][v]);
-      Oi[b] = i32x4{0, 0, 0, 0};
+      for (int v = 0; v < 4; ++v) Of[c][b][v] += ldexpf((float)Oi[c][b][v], F[c] - 7 * (t_dig + 1));
+      Oi[c][b] = i32x4{0, 0, 0, 0};
     }
-    since_flush = 0;
+    since_flush[c] = 0;
   };
 
   auto compute = [&](int idx, bool valid, const Tile& T) {
@@ -260,9 +278,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     // the previous tile's reads of the slot were consumed before this point.
 #pragma unroll
     for (int u = 0; u < VCH; ++u) {
-      const int F = 64 * u + lane;
-      const int r = F / NC16;
-      *reinterpret_cast<u32x4*>(slot + r * D + 16 * ((F % NC16) ^ dswz<SP>(r))) = T.v[u];
+      const int Fc = 64 * u + lane;
+      const int r = Fc / NC16;
+      *reinterpret_cast<u32x4*>(slot + r * D + 16 * ((Fc % NC16) ^ dswz<SP>(r))) = T.v[u];
     }
 #pragma unroll
     for (int e = 0; e < NSC; ++e) reinterpret_cast<float*>(slot + KT * D)[64 * e + lane] = T.sc[e];
@@ -284,86 +302,93 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     const bool tail = !valid || k0 + KT > a.s_k;
     const int key_lim = valid ? last_key - k0 - KG * hq : -1;   // key KG hq + j is visible iff j <= key_lim
 
-    // S^T: block kb, C-row 4 hq + v = key KG hq + 4 kb + v; A row n = key KG (n/4) + 4 kb + n%4
-    float s[KB][4];
+    i32x4 pdig[NS];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      i32x4 acc = {0, 0, 0, 0};
+    for (int c = 0; c < NS; ++c) {
+      // S^T: block kb, C-row 4 hq + v = key KG hq + 4 kb + v; A row n = key KG (n/4) + 4 kb + n%4
+      float s[KB][4];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) acc = mfma16_i8(T.k[kb][kk], qdig[kk], acc);
+      for (int kb = 0; kb < KB; ++kb) {
+        i32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float y = (float)acc[v] * s_comb;
-        y = y + dpp_row_ror<8>(y);
-        y = y + dpp_row_ror<4>(y);
-        s[kb][v] = y * ks[kb][v];
+        for (int kk = 0; kk < NKK; ++kk) acc = mfma16_i8(T.k[kb][kk], qdig[c][kk], acc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float y = (float)acc[v] * s_comb[c];
+          y = y + dpp_row_ror<8>(y);
+          y = y + dpp_row_ror<4>(y);
+          s[kb][v] = y * ks[kb][v];
+        }
       }
-    }
-    if (tail) {
+      if (tail) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (4 * kb + v > key_lim) s[kb][v] = neg_inf();
+      }
+      float mx = neg_inf();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (4 * kb + v > key_lim) s[kb][v] = neg_inf();
-    }
-    float mx = neg_inf();
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      const bool raised = __any(mx - m_run[c] > lazy_thr);   // wave-uniform
+      if (raised) {
+        flush(c);
+        const float m_new = fmaxf(m_run[c], mx);
+        const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run[c] - m_use) * c2);
+        l_run[c] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    if (__any(mx - m_run > lazy_thr)) {
-      flush();
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Of[b][v] *= alpha;
-      m_run = m_new;
-      mc = m_use * c2;
-    }
-    float pt[KB][4];
-    float ps = 0.f, pmax = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], c2, -mc));
-        ps += p;
-        pt[kb][v] = p * vs[kb][v];
-        pmax = fmaxf(pmax, pt[kb][v]);
+          for (int v = 0; v < 4; ++v) Of[c][b][v] *= alpha;
+        m_run[c] = m_new;
+        mc[c] = m_use * c2;
       }
-    l_run += ps;
-    pmax = max_xor16(pmax);
-    pmax = max_xor32(pmax);
-    int Fp = -1000;
-    if (pmax > 0.f) (void)frexpf(pmax, &Fp);    // pmax < 2^Fp
-    if (__any(Fp > F) || since_flush >= kFlushTiles) {
-      flush();
-      if (Fp > F) F = Fp + 1;                  // one octave of headroom for later tiles
-    }
-    ++since_flush;
-    // digit t of x = P~ / 2^F in [0, 1) is bits 0..6 of floor(x 2^(7t+7)) (exact: the product
-    // is a power-of-two scaling and x < 1 keeps it below 2^28); k-slot 4 kb + v of lane group
-    // hq is key KG hq + 4 kb + v
-    const float to_int = ldexpf(1.f, 7 * t_dig + 7 - F);
-    unsigned pw[4] = {0u, 0u, 0u, 0u};
+      float pt[KB][4];
+      float ps = 0.f, pmax = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      unsigned w = 0;
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) w |= (((unsigned)(pt[kb][v] * to_int)) & 0xffu) << (8 * v);
-      pw[kb] = w & 0x7f7f7f7fu;
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], c2, -mc[c]));
+          ps += p;
+          pt[kb][v] = p * vs[kb][v];
+          pmax = fmaxf(pmax, pt[kb][v]);
+        }
+      l_run[c] += ps;
+      pmax = max_xor16(pmax);
+      pmax = max_xor32(pmax);
+      int Fp = -1000;
+      if (pmax > 0.f) (void)frexpf(pmax, &Fp);    // pmax < 2^Fp
+      const bool grow = __any(Fp > F[c]) || since_flush[c] >= kFlushTiles;   // wave-uniform
+      if (grow && !raised) flush(c);
+      if (raised || grow) F[c] = Fp + 1;          // Oi is empty: restart the scale, one octave of headroom
+      ++since_flush[c];
+      // x = P~ / 2^F lies in [0, 1): Q = rint(x 2^28) < 2^28 is x to 28 fractional bits, rounded
+      // to nearest (the scaling by a power of two is exact), and digit t of x is bits
+      // 21 - 7t .. 27 - 7t of Q.  k-slot 4 kb + v of lane group hq is key KG hq + 4 kb + v.
+      const int sh = 21 - 7 * t_dig;
+      unsigned pw[4] = {0u, 0u, 0u, 0u};   // k-slots past the tile's keys stay zero
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        unsigned w = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const unsigned qx = (unsigned)__builtin_rintf(ldexpf(pt[kb][v], 28 - F[c]));
+          w |= ((qx >> sh) & 0x7fu) << (8 * v);
+        }
+        pw[kb] = w;
+      }
+      pdig[c] = i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
     }
-    const i32x4 pdig = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
 
-    // O^T block b (head-dim 16 b + row): A = V^T via transposing reads.  As a source lane, n
-    // addresses key row KG hq + 8 h8 + n/2, bytes 16 b + 8 (n%2) .. + 8; lane n then receives
-    // keys KG hq + 8 h8 + 0..7 of head-dim 16 b + n.
+    // O^T block b (head-dim 16 b + row): A = V^T via transposing reads, shared by the column
+    // sets.  As a source lane, n addresses key row KG hq + 8 h8 + n/2, bytes 16 b + 8 (n%2) .. + 8;
+    // lane n then receives keys KG hq + 8 h8 + 0..7 of head-dim 16 b + n.
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       int w4[4] = {0, 0, 0, 0};
@@ -376,7 +401,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         w4[2 * h8 + 1] = r[1];
       }
       const i32x4 vt = {w4[0], w4[1], w4[2], w4[3]};
-      Oi[b] = mfma16_i8(vt, pdig, Oi[b]);
+#pragma unroll
+      for (int c = 0; c < NS; ++c) Oi[c][b] = mfma16_i8(vt, pdig[c], Oi[c][b]);
     }
   };
 
@@ -400,33 +426,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   }
 
   // ---- combine digit columns (O) and lane groups (l), then the waves through LDS
-  flush();
-  float O[NB][4];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) O[b][v] = Of[b][v];
-  float lt = l_run;
-  lt = add_xor16(lt);
-  lt = add_xor32(lt);
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float y = O[b][v];
-      y = y + dpp_row_ror<8>(y);
-      y = y + dpp_row_ror<4>(y);
-      O[b][v] = y;
+  for (int c = 0; c < NS; ++c) {
+    flush(c);
+    float lt = l_run[c];
+    lt = add_xor16(lt);
+    lt = add_xor32(lt);
+    if (lane == gq) {  // t_dig == 0, hq == 0
+      lds_m[wave][4 * c + gq] = m_run[c];
+      lds_l[wave][4 * c + gq] = lt;
     }
-  if (lane == gq) {  // t_dig == 0, hq == 0
-    lds_m[wave][gq] = m_run;
-    lds_l[wave][gq] = lt;
-  }
-  if (t_dig == 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) lds_o[wave][gq][16 * b + 4 * hq + v] = O[b][v];
+      for (int v = 0; v < 4; ++v) {
+        float y = Of[c][b][v];
+        y = y + dpp_row_ror<8>(y);
+        y = y + dpp_row_ror<4>(y);
+        if (t_dig == 0) lds_o[wave][4 * c + gq][16 * b + 4 * hq + v] = y;
+      }
   }
   __syncthreads();
 
@@ -497,34 +515,44 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[head] = L > 0.f ? M * a.scale + logf(L) : neg_inf();
 }
 
-template <int D>
+template <int D, int NS>
 hipError_t launch_d(const DecodeArgs& a_in, hipStream_t st, const char** name) {
   DecodeArgs a = a_in;
   constexpr int KT = DCfg<D>::KT;
   const int tiles = (a.s_k - a.key_lo + KT - 1) / KT;
   a.tiles_per_split = (tiles + a.num_splits - 1) / a.num_splits;
-  const dim3 grid((unsigned)a.num_splits, (unsigned)a.bh_kv, (unsigned)((a.group + 3) / 4));
-  hipLaunchKernelGGL((decode_partial_kernel<D>), grid, dim3(64 * kWaves), 0, st, a);
+  const int hpw = 4 * NS;
+  const dim3 grid((unsigned)a.num_splits, (unsigned)a.bh_kv, (unsigned)((a.group + hpw - 1) / hpw));
+  hipLaunchKernelGGL((decode_partial_kernel<D, NS>), grid, dim3(64 * kWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.bh_q), dim3(64), 0, st, a);
-  *name = "decode_int8";
+  *name = NS == 2 ? "decode_int8_h8" : "decode_int8";
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_hd(const DecodeArgs& a, hipStream_t st, const char** name) {
+  if constexpr (D <= 128) {
+    if (decode_heads_per_workgroup(a.group, D) == 8) return launch_d<D, 2>(a, st, name);
+  }
+  return launch_d<D, 1>(a, st, name);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, const char** name) {
-  if (a.bh_kv > 65535 || (a.group + 3) / 4 > 65535) return hipErrorInvalidConfiguration;
+  const int hpw = decode_heads_per_workgroup(a.group, d);
+  if (a.bh_kv > 65535 || (a.group + hpw - 1) / hpw > 65535) return hipErrorInvalidConfiguration;
   switch (d) {
-    case 32: return launch_d<32>(a, stream, name);
-    case 64: return launch_d<64>(a, stream, name);
-    case 96: return launch_d<96>(a, stream, name);
-    case 128: return launch_d<128>(a, stream, name);
-    case 160: return launch_d<160>(a, stream, name);
-    case 192: return launch_d<192>(a, stream, name);
-    case 224: return launch_d<224>(a, stream, name);
-    case 256: return launch_d<256>(a, stream, name);
+    case 32: return launch_hd<32>(a, stream, name);
+    case 64: return launch_hd<64>(a, stream, name);
+    case 96: return launch_hd<96>(a, stream, name);
+    case 128: return launch_hd<128>(a, stream, name);
+    case 160: return launch_hd<160>(a, stream, name);
+    case 192: return launch_hd<192>(a, stream, name);
+    case 224: return launch_hd<224>(a, stream, name);
+    case 256: return launch_hd<256>(a, stream, name);
     default: return hipErrorInvalidValue;
   }
 }

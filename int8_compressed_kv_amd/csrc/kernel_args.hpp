@@ -92,6 +92,10 @@ struct TqArgs {
   float cb[16];           // decode: the 2^bits centroids, ascending
 };
 
+// Query heads one decode workgroup serves: 8 (two MFMA column sets) for groups of more than 4
+// heads at head_dim <= 128, else 4.  The split count and the grid both follow it.
+inline int decode_heads_per_workgroup(int group, int head_dim) { return (group > 4 && head_dim <= 128) ? 8 : 4; }
+
 // Launchers return hipSuccess or the launch error; *name receives the instantiation name.
 hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d,
                            int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);

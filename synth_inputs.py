@@ -26,7 +26,8 @@ import dataclasses
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "draw_qkv", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "round_bf16", "rng_normal", "random_signs"]
+           "bf16_bits_to_f32", "round_bf16", "rng_normal", "random_signs", "score_profile",
+           "decode_profile_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -111,3 +112,40 @@ def random_signs(seed: int, n: int) -> np.ndarray:
     rotation draws, passed to both the oracle and the library as an input."""
     g = np.random.Generator(np.random.PCG64(seed))
     return np.where(g.random(n) < 0.5, -1, 1).astype(np.int8)
+
+
+def score_profile(kind: str, s_k: int) -> np.ndarray:
+    """Per-key offsets a_j (in nats) that decode_profile_inputs adds to the scores of a cache:
+      "sink12", "sink16"  key 0 sits 12 / 16 nats above the rest (an attention sink);
+      "rising"            the offset climbs linearly from 0 to 30 nats over the cache (recency);
+      "step"              0 for the first third, 7 octaves (7 ln 2 nats) for the second, and
+                          20 nats more for the last third.
+      "flat"              all zero."""
+    a = np.zeros(s_k, np.float64)
+    if kind in ("sink12", "sink16"):
+        a[0] = float(kind[4:])
+    elif kind == "rising":
+        a = np.linspace(0.0, 30.0, s_k)
+    elif kind == "step":
+        a[s_k // 3:] = 7.0 * np.log(2.0)
+        a[2 * s_k // 3:] += 20.0
+    elif kind != "flat":
+        raise ValueError(kind)
+    return a
+
+
+def decode_profile_inputs(seed: int, bh_kv: int, group: int, s_k: int, d: int, kind: str, v_mean: float = 0.5):
+    """Decode inputs whose scores follow a profile: the query heads of a KV head share a random
+    direction w (q_h = w + 0.25 z_h, rounded to bf16) and key j is z_j + a_j sqrt(d) w / |w|^2, so
+    its score q_h . k_j / sqrt(d) is about a_j plus a unit-variance term.  V has channel mean
+    v_mean.  Returns q (bh_kv*group, 1, d) bf16-valued float32, k and v (bh_kv, s_k, d) float32."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    a = score_profile(kind, s_k)
+    w = g.standard_normal(size=(bh_kv, d), dtype=np.float32)
+    zq = g.standard_normal(size=(bh_kv, group, d), dtype=np.float32)
+    q = round_bf16((w[:, None, :] + np.float32(0.25) * zq).reshape(bh_kv * group, 1, d))
+    k = g.standard_normal(size=(bh_kv, s_k, d), dtype=np.float32)
+    dirn = (np.sqrt(d) * w / (w * w).sum(axis=1, keepdims=True)).astype(np.float32)
+    k += (a[None, :, None] * dirn[:, None, :]).astype(np.float32)
+    v = g.standard_normal(size=(bh_kv, s_k, d), dtype=np.float32) + np.float32(v_mean)
+    return q, k, v

@@ -112,3 +112,42 @@ def test_decode_extreme_scales():
     ref, _ = oracle.decode(q, kq, vq, k_scale=ks, v_scale=vs)
     scale = np.abs(ref).max()
     check_close(to_np(out) / scale, ref / scale, TOL_F32, "relative to max |out|")
+
+
+@pytest.mark.parametrize("kind", ["sink12", "sink16", "rising", "step"])
+@pytest.mark.parametrize("group", [4, 8])
+def test_decode_long_cache_score_profiles_absolute(kind, group):
+    """32768 keys with a non-zero-mean V (channel mean 0.5) and the score profiles that stress
+    the P~ V digit scale: an attention sink 12 / 16 nats above the rest, scores rising 0 -> 30
+    nats over the cache, and a 7-octave step (below the lazy-raise threshold) followed by a
+    20-nat step (a raise).  Checked at an absolute 1e-5 against the dequantized oracle, in the
+    split count the long-cache workload uses (2 per KV head at 128 KV heads) and the automatic one."""
+    import int8_compressed_kv_amd as fa
+    from synth_inputs import decode_profile_inputs
+    torch_gpu()
+    bh_kv, s_k, d = 4, 32768, 128
+    say(f"decode profile={kind} G={group} s_k={s_k}")
+    q, k, v = decode_profile_inputs(700 + group, bh_kv, group, s_k, d, kind)
+    dev, (kq, ks, vq, vs) = _cache(k, v)
+    ref, lref = oracle.decode(q, kq, vq, k_scale=ks, v_scale=vs)
+    for splits in (2, 0):
+        out, lse = fa.decode(to_dev(q, "bf16"), *dev, num_splits=splits, return_lse=True)
+        check_close(to_np(out), ref, TOL_F32, f"{kind} G={group} splits={splits}")
+        check_close(to_np(lse), lref[:, 0], TOL_F32 * max(1.0, float(np.abs(lref).max())), "lse")
+    assert fa.last_kernel() == ("decode_int8_h8" if group == 8 else "decode_int8")
+
+
+def test_decode_group8_reads_the_cache_with_one_workgroup_set():
+    """G = 8 at head_dim 128: one workgroup serves all 8 query heads of its KV head (grid z = 1),
+    and the split count matches G = 4 for the same number of KV heads."""
+    import int8_compressed_kv_amd as fa
+    torch_gpu()
+    assert fa.decode_num_splits(8 * 128, 128, 32768, 128) == fa.decode_num_splits(4 * 128, 128, 32768, 128)
+    q, k, v = rng_normal(710, (16, 1, 128), (2, 3000, 128), (2, 3000, 128))
+    q = round_bf16(q)
+    dev, (kq, ks, vq, vs) = _cache(k, v)
+    ref, _ = oracle.decode(q, kq, vq, k_scale=ks, v_scale=vs)
+    for splits in (0, 1, 5):
+        out = fa.decode(to_dev(q, "bf16"), *dev, num_splits=splits)
+        check_close(to_np(out), ref, TOL_F32, f"G=8 splits={splits}")
+        assert fa.last_kernel() == "decode_int8_h8"
