@@ -163,6 +163,21 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _same_device(ref, **tensors):
+    """Every named tensor (None skipped) must sit on ref's device."""
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _want(t, name, shape, dtype):
+    """t must have exactly this shape and dtype (a caller buffer the kernels read or write)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
@@ -205,6 +220,7 @@ def compress_kv(x, out=None, scales=None):
         raise ValueError("codes output must be int8 with the input's shape")
     if scales.dtype != torch.float32 or scales.shape != x.shape[:-1]:
         raise ValueError("scales output must be fp32 with the input's leading shape")
+    _same_device(x, codes=out, scales=scales)
     _check(lib().fa_compress_kv(_dev(x, "x"), _dtype_code(x), n, d, _dev(out, "codes"),
                                 _dev(scales, "scales"), _stream()))
     return out, scales
@@ -229,6 +245,7 @@ def append_kv(k_new, v_new, pos, k_cache, v_cache, k_scale, v_scale):
         raise ValueError("scales must be fp32")
     if pos.dtype != torch.int32 or tuple(pos.shape) != (bh_kv,):
         raise ValueError("pos must be an int32 tensor of shape (bh_kv,)")
+    _same_device(k_new, v_new=v_new, pos=pos, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale)
     _check(lib().fa_append_kv(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new), bh_kv, n_new, d,
                               _dev(pos, "pos"), cap, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                               _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream()))
@@ -253,11 +270,17 @@ def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(),
         raise ValueError("k and v must share a dtype")
     if (k_scale is None) != (v_scale is None):
         raise ValueError("give both k_scale and v_scale, or neither")
-    if k_scale is not None and (tuple(k_scale.shape) != (bh_kv, s_k) or tuple(v_scale.shape) != (bh_kv, s_k)):
-        raise ValueError("scales must have shape (bh_kv, s_k)")
+    if k_scale is not None:
+        _want(k_scale, "k_scale", (bh_kv, s_k), torch.float32)
+        _want(v_scale, "v_scale", (bh_kv, s_k), torch.float32)
+    if (k.dtype == torch.int8) != (k_scale is not None):
+        raise ValueError("int8 k, v need k_scale and v_scale; other dtypes take none")
     odt = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((bh_q, s_q, d), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (bh_q, s_q, d):
+        raise ValueError(f"out must have shape {(bh_q, s_q, d)}, got {tuple(out.shape)}")
+    _same_device(q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out)
     lse = torch.empty((bh_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
     epi, n_epi = _epilogue(epilogue, d)
     _check(lib().fa_forward(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dtype_code(k),
@@ -290,10 +313,16 @@ def tq_encode(x, signs, bits, codebook, codes=None, norms=None):
     n = x.numel() // d if d else 0
     if signs.dtype != torch.int8 or tuple(signs.shape) != (d,):
         raise ValueError("signs must be an int8 tensor of shape (head_dim,)")
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
+    cshape = tuple(x.shape[:-1]) + (d * bits // 8,)
     if codes is None:
-        codes = torch.empty(tuple(x.shape[:-1]) + (d * bits // 8,), dtype=torch.uint8, device=x.device)
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if norms is None:
         norms = torch.empty(tuple(x.shape[:-1]), dtype=torch.float32, device=x.device)
+    _want(codes, "codes", cshape, torch.uint8)
+    _want(norms, "norms", tuple(x.shape[:-1]), torch.float32)
+    _same_device(x, signs=signs, codes=codes, norms=norms)
     cb, cbp = _host_f32(codebook)
     _check(lib().fa_tq_encode(_dev(x, "x"), _dtype_code(x), n, d, int(bits), _dev(signs, "signs"), cbp,
                               _dev(codes, "codes"), _dev(norms, "norms"), _stream()))
@@ -303,13 +332,22 @@ def tq_encode(x, signs, bits, codebook, codes=None, norms=None):
 def tq_decode(codes, norms, signs, bits, codebook, out_dtype=None, out=None):
     """Rows (..., head_dim) decoded from TurboQuant codes and norms (fp32 by default)."""
     torch = _torch()
+    if signs.dim() != 1 or signs.dtype != torch.int8:
+        raise ValueError("signs must be an int8 tensor of shape (head_dim,)")
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
     d = signs.shape[0]
-    if codes.dtype != torch.uint8 or codes.shape[-1] != d * bits // 8:
+    if codes.dtype != torch.uint8 or codes.dim() < 1 or codes.shape[-1] != d * bits // 8:
         raise ValueError("codes must be uint8 (..., head_dim * bits / 8)")
+    lead = tuple(codes.shape[:-1])
+    _want(norms, "norms", lead, torch.float32)
     n = norms.numel()
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty(tuple(codes.shape[:-1]) + (d,), dtype=odt, device=codes.device)
+        out = torch.empty(lead + (d,), dtype=odt, device=codes.device)
+    elif tuple(out.shape) != lead + (d,):
+        raise ValueError(f"out must have shape {lead + (d,)}, got {tuple(out.shape)}")
+    _same_device(codes, norms=norms, signs=signs, out=out)
     cb, cbp = _host_f32(codebook)
     _check(lib().fa_tq_decode(_dev(codes, "codes"), _dev(norms, "norms"), n, d, int(bits), _dev(signs, "signs"),
                               cbp, _dev(out, "out"), _out_code(out.dtype), _stream()))
@@ -333,6 +371,7 @@ def merge_lse(o_parts, lse_parts, *, epilogue=(), out_dtype=None, out=None, retu
         out = torch.empty(tuple(o_parts.shape[1:]), dtype=odt, device=o_parts.device)
     if tuple(out.shape) != tuple(o_parts.shape[1:]):
         raise ValueError("out must have the shape of one part")
+    _same_device(o_parts, lse_parts=lse_parts, out=out)
     lse = torch.empty(tuple(lse_parts.shape[1:]), dtype=torch.float32, device=o_parts.device) if return_lse else None
     epi, n_epi = _epilogue(epilogue, d)
     _check(lib().fa_merge_lse(_dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts"), n_parts, rows, d,
@@ -361,11 +400,14 @@ def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epi
         raise ValueError("k and v must have shape (bh_kv, s_k, head_dim)")
     if k.dtype != torch.int8 or v.dtype != torch.int8:
         raise ValueError("decode reads the int8 cache: k and v must be int8 codes")
-    if tuple(k_scale.shape) != (bh_kv, s_k) or tuple(v_scale.shape) != (bh_kv, s_k):
-        raise ValueError("scales must have shape (bh_kv, s_k)")
+    _want(k_scale, "k_scale", (bh_kv, s_k), torch.float32)
+    _want(v_scale, "v_scale", (bh_kv, s_k), torch.float32)
     odt = torch.float32 if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((bh_q, 1, d), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (bh_q, 1, d):
+        raise ValueError(f"out must have shape {(bh_q, 1, d)}, got {tuple(out.shape)}")
+    _same_device(q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, workspace=workspace)
     need = decode_workspace_bytes(bh_q, bh_kv, s_k, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -377,3 +419,4 @@ def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epi
                            epi, n_epi, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                            _stream()))
     return (out, lse) if return_lse else out
+

@@ -238,3 +238,43 @@ def test_tq_rejects_bad_codebook_and_pointers(L):
             assert np.array_equal(cb, -cb[::-1]), "the host codebook is not exactly antisymmetric"
     assert L.fa_tq_encode(vp(0), 0, 0, 64, 2, vp(0), vp(good.ctypes.data), vp(0), vp(0), None) == 0
     assert L.fa_tq_decode(vp(1 << 20), vp(1 << 20), 4, 64, 2, vp(1 << 20), vp(good.ctypes.data), vp(1 << 20), 2, None) == -2
+
+
+@pytest.mark.parametrize("case", ["fwd_out_shape", "fwd_scale_dtype", "fwd_scale_shape", "fwd_scale_missing",
+                                  "dec_out_shape", "dec_scale_dtype", "tqd_norms_rows", "tqd_out_shape",
+                                  "tqe_codes_shape", "tqe_norms_dtype", "tqe_bits", "merge_out_shape"])
+def test_python_layer_checks_caller_buffers_before_any_launch(case):
+    """Undersized or wrongly typed caller buffers are refused with ValueError by the binding;
+    the messages name the offending buffer, so these fire before the device check that CPU
+    tensors would otherwise hit."""
+    torch = pytest.importorskip("torch")
+    z = torch.zeros
+    q, k, v = z(4, 8, 64), z(2, 16, 64), z(2, 16, 64)
+    k8, v8 = z(2, 16, 64, dtype=torch.int8), z(2, 16, 64, dtype=torch.int8)
+    ks, vs = z(2, 16), z(2, 16)
+    q1 = z(4, 1, 64)
+    signs = torch.ones(64, dtype=torch.int8)
+    calls = {
+        "fwd_out_shape": (lambda: fa.flash_attention(q, k, v, out=z(4, 7, 64)), "out must have shape"),
+        "fwd_scale_dtype": (lambda: fa.flash_attention(q, k8, v8, k_scale=ks.double(), v_scale=vs), "k_scale must be"),
+        "fwd_scale_shape": (lambda: fa.flash_attention(q, k8, v8, k_scale=z(2, 15), v_scale=vs), "k_scale must have shape"),
+        "fwd_scale_missing": (lambda: fa.flash_attention(q, k8, v8), "need k_scale"),
+        "dec_out_shape": (lambda: fa.decode(q1, k8, v8, ks, vs, out=z(4, 2, 64)), "out must have shape"),
+        "dec_scale_dtype": (lambda: fa.decode(q1, k8, v8, ks, vs.half()), "v_scale must be"),
+        "tqd_norms_rows": (lambda: fa.tq_decode(z(5, 32, dtype=torch.uint8), z(4), signs, 4, [0.0] * 16), "norms must have shape"),
+        "tqd_out_shape": (lambda: fa.tq_decode(z(5, 32, dtype=torch.uint8), z(5), signs, 4, [0.0] * 16, out=z(4, 64)), "out must have shape"),
+        "tqe_codes_shape": (lambda: fa.tq_encode(z(5, 64), signs, 4, [0.0] * 16, codes=z(5, 16, dtype=torch.uint8)), "codes must have shape"),
+        "tqe_norms_dtype": (lambda: fa.tq_encode(z(5, 64), signs, 4, [0.0] * 16, norms=z(5, dtype=torch.float64)), "norms must be"),
+        "tqe_bits": (lambda: fa.tq_encode(z(5, 64), signs, 5, [0.0] * 32), "bits must be"),
+        "merge_out_shape": (lambda: fa.merge_lse(z(3, 10, 64), z(3, 10), out=z(9, 64)), "out must have the shape"),
+    }
+    fn, msg = calls[case]
+    with pytest.raises(ValueError, match=msg):
+        fn()
+
+
+def test_python_layer_checks_devices():
+    torch = pytest.importorskip("torch")
+    q, k, v = torch.zeros(4, 8, 64), torch.zeros(2, 16, 64), torch.zeros(2, 16, 64, device="meta")
+    with pytest.raises(ValueError, match="v is on meta"):
+        fa.flash_attention(q, k, v)
