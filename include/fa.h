@@ -231,6 +231,28 @@ int fa_decode(const void* q, int32_t q_dtype,
               const fa_epilogue_op* epi, int32_t n_epi,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_noalloc -- fa_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as fa_decode (bit for bit
+ * at the same num_splits), except that the partial (m, l, O) states go to a fixed device array
+ * inside the library, fa_decode_noalloc_max_bytes() bytes (4 MiB) per GPU, held from the first
+ * call on that GPU until the process ends.  The states need bh_q * splits * (head_dim + 2) * 4
+ * bytes; a call needing more returns FA_ERR_WORKSPACE and enqueues nothing.  `stream` must belong
+ * to the current device (FA_ERR_INVALID otherwise).  Every call on one GPU shares that GPU's
+ * array: calls whose kernels may overlap (concurrent streams on one GPU) race and must be
+ * serialised by the caller.  The caller still provides q, the cache, out and lse_out.
+ */
+int fa_decode_noalloc(const void* q, int32_t q_dtype,
+                      const int8_t* k, const int8_t* v, const float* k_scale, const float* v_scale,
+                      void* out, int32_t out_dtype, float* lse_out,
+                      int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim,
+                      float softmax_scale, int32_t window, int32_t num_splits,
+                      const fa_epilogue_op* epi, int32_t n_epi, void* stream);
+
+/* Size in bytes of the fixed scratch array fa_decode_noalloc uses on each GPU. */
+size_t fa_decode_noalloc_max_bytes(void);
+
 /* Text for the last non-OK return on the calling thread ("" if none).  Valid until the
  * next library call on this thread. */
 const char* fa_last_error(void);

@@ -26,7 +26,7 @@ import os
 from dataclasses import dataclass
 
 __all__ = ["Mul", "Add", "Bias", "ReLU", "compress_kv", "append_kv", "tq_codebook", "tq_encode", "tq_decode", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
-           "decode_num_splits", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
+           "decode_num_splits", "decode_noalloc", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
            "F32", "BF16", "I8"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -105,6 +105,11 @@ def lib() -> ctypes.CDLL:
     L.fa_decode.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32, i32, i32,
                             ctypes.POINTER(_EpiOp), i32, vp, ctypes.c_size_t, vp]
     L.fa_decode.restype = ctypes.c_int
+    L.fa_decode_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32, i32, i32,
+                                    ctypes.POINTER(_EpiOp), i32, vp]
+    L.fa_decode_noalloc.restype = ctypes.c_int
+    L.fa_decode_noalloc_max_bytes.argtypes = []
+    L.fa_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     L.fa_last_error.argtypes = []
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_last_kernel.argtypes = []
@@ -420,3 +425,30 @@ def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epi
                            _stream()))
     return (out, lse) if return_lse else out
 
+
+def decode_noalloc(q, k, v, k_scale, v_scale, out, *, lse=None, window=0, scale=None, num_splits=0, epilogue=()):
+    """decode() through fa_decode_noalloc: the partial states go to the library's fixed device
+    scratch array, and nothing is allocated here either, so the caller passes `out` (bh_q, 1, d)
+    (and optionally `lse` (bh_q,) fp32).  Calls that may overlap on one GPU race on that array."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[1] != 1:
+        raise ValueError("q must have shape (bh_q, 1, head_dim)")
+    bh_q, _, d = q.shape
+    bh_kv, s_k, dk = k.shape
+    if dk != d or tuple(v.shape) != (bh_kv, s_k, d):
+        raise ValueError("k and v must have shape (bh_kv, s_k, head_dim)")
+    if k.dtype != torch.int8 or v.dtype != torch.int8:
+        raise ValueError("decode reads the int8 cache: k and v must be int8 codes")
+    _want(k_scale, "k_scale", (bh_kv, s_k), torch.float32)
+    _want(v_scale, "v_scale", (bh_kv, s_k), torch.float32)
+    if tuple(out.shape) != (bh_q, 1, d):
+        raise ValueError(f"out must have shape {(bh_q, 1, d)}, got {tuple(out.shape)}")
+    if lse is not None:
+        _want(lse, "lse", (bh_q,), torch.float32)
+    _same_device(q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse)
+    epi, n_epi = _epilogue(epilogue, d)
+    _check(lib().fa_decode_noalloc(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dev(k_scale, "k_scale"),
+                                   _dev(v_scale, "v_scale"), _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"),
+                                   bh_q, bh_kv, s_k, d, float(scale) if scale else 0.0, int(window), int(num_splits),
+                                   epi, n_epi, _stream()))
+    return out

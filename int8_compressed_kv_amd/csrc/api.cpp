@@ -334,10 +334,17 @@ size_t fa_decode_workspace_bytes(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32
   return (size_t)bh_q * (size_t)num_splits * (size_t)(head_dim + 2) * sizeof(float);
 }
 
-int fa_decode(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, const float* k_scale,
-              const float* v_scale, void* out, int32_t out_dtype, float* lse_out, int32_t bh_q, int32_t bh_kv,
-              int32_t s_k, int32_t head_dim, float softmax_scale, int32_t window, int32_t num_splits,
-              const fa_epilogue_op* epi, int32_t n_epi, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_decode and fa_decode_noalloc: the same checks and kernels; `noalloc` selects the library's
+// fixed scratch array instead of the caller's workspace.
+int decode_impl(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, const float* k_scale,
+                const float* v_scale, void* out, int32_t out_dtype, float* lse_out, int32_t bh_q, int32_t bh_kv,
+                int32_t s_k, int32_t head_dim, float softmax_scale, int32_t window, int32_t num_splits,
+                const fa_epilogue_op* epi, int32_t n_epi, void* workspace, size_t workspace_bytes, bool noalloc,
+                void* stream) {
   g_last_error.clear();
   if (int r = check_head_dim(head_dim)) return r;
   if (bh_q <= 0 || bh_kv <= 0) return fail(FA_ERR_INVALID, "bh_q and bh_kv must be positive");
@@ -358,10 +365,26 @@ int fa_decode(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, 
   if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)) return fail(FA_ERR_INVALID, "lse_out must be 4-byte aligned");
   const int32_t splits = num_splits > 0 ? num_splits : fa_decode_num_splits(bh_q, bh_kv, s_k, head_dim);
   const size_t need = (size_t)bh_q * (size_t)splits * (size_t)(head_dim + 2) * sizeof(float);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
-                workspace ? "" : ", NULL");
-  if (!aligned16(workspace)) return fail(FA_ERR_INVALID, "workspace must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (noalloc) {
+    if (need > fa::kDecodeScratchBytes)
+      return fail(FA_ERR_WORKSPACE, "decode partial states need %zu bytes, above the %zu-byte scratch of "
+                  "fa_decode_noalloc (fewer splits or heads per call, or fa_decode with a workspace)",
+                  need, fa::kDecodeScratchBytes);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const int sdev = hipGetStreamDeviceId(st);
+    if (sdev != dev)
+      return fail(FA_ERR_INVALID, "the stream belongs to device %d but device %d is current", sdev, dev);
+    e = fa::decode_scratch_address(dev, &workspace);
+    if (e != hipSuccess) return hip_fail(e, "decode scratch address");
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                  workspace ? "" : ", NULL");
+    if (!aligned16(workspace)) return fail(FA_ERR_INVALID, "workspace must be 16-byte aligned");
+  }
 
   fa::DecodeArgs a;
   a.q = q;
@@ -386,10 +409,32 @@ int fa_decode(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, 
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.epi = ea;
   const char* name = "";
-  hipError_t e = fa::launch_decode(a, head_dim, static_cast<hipStream_t>(stream), &name);
+  hipError_t e = fa::launch_decode(a, head_dim, st, &name);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   g_last_kernel = name;
   return FA_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, const float* k_scale,
+              const float* v_scale, void* out, int32_t out_dtype, float* lse_out, int32_t bh_q, int32_t bh_kv,
+              int32_t s_k, int32_t head_dim, float softmax_scale, int32_t window, int32_t num_splits,
+              const fa_epilogue_op* epi, int32_t n_epi, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_dtype, k, v, k_scale, v_scale, out, out_dtype, lse_out, bh_q, bh_kv, s_k, head_dim,
+                     softmax_scale, window, num_splits, epi, n_epi, workspace, workspace_bytes, false, stream);
+}
+
+int fa_decode_noalloc(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v, const float* k_scale,
+                      const float* v_scale, void* out, int32_t out_dtype, float* lse_out, int32_t bh_q,
+                      int32_t bh_kv, int32_t s_k, int32_t head_dim, float softmax_scale, int32_t window,
+                      int32_t num_splits, const fa_epilogue_op* epi, int32_t n_epi, void* stream) {
+  return decode_impl(q, q_dtype, k, v, k_scale, v_scale, out, out_dtype, lse_out, bh_q, bh_kv, s_k, head_dim,
+                     softmax_scale, window, num_splits, epi, n_epi, nullptr, 0, true, stream);
+}
+
+size_t fa_decode_noalloc_max_bytes(void) { return fa::kDecodeScratchBytes; }
 
 }  // extern "C"

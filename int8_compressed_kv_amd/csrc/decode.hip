@@ -40,10 +40,35 @@
 //     g of the score accumulator owns keys (KT/4) g .. (KT/4) g + KT/4 - 1 -- exactly the keys
 //     the transposing read gives that lane group for the P~ V product.
 //   * The online softmax (running max raised lazily, as in the prefill kernel) runs in fp32.
+#include <mutex>
+
 #include "device_common.hpp"
 
 namespace fa {
 
+// Fixed scratch for the allocation-free decode entry point: the partial (m, l, O) states of
+// every (query head, split), each written in full by the partial pass before the merge pass
+// reads it, so nothing needs clearing between calls.  Host code never uses the array's name as
+// an address (on the host it is only a stand-in); it uses the per-device address from
+// hipGetSymbolAddress below.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch_address(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 namespace {
 
 constexpr float kLazyLog2 = 8.0f;

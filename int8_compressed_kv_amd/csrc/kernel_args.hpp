@@ -96,6 +96,9 @@ struct TqArgs {
 // heads at head_dim <= 128, else 4.  The split count and the grid both follow it.
 inline int decode_heads_per_workgroup(int group, int head_dim) { return (group > 4 && head_dim <= 128) ? 8 : 4; }
 
+// Size of the fixed device scratch array fa_decode_noalloc keeps its partial states in.
+constexpr size_t kDecodeScratchBytes = size_t(4) << 20;
+
 // Launchers return hipSuccess or the launch error; *name receives the instantiation name.
 hipError_t launch_compress(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t d,
                            int8_t* q_out, float* scale_out, hipStream_t stream, const char** name);
@@ -105,6 +108,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int32_t d, int32_t kv_dtype,
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_prefill_i8kv(const PrefillArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, const char** name);
+// Device address of this device's copy of the decode scratch array (looked up once per device,
+// then cached); `device` must be the current device.
+hipError_t decode_scratch_address(int device, void** ptr);
 hipError_t launch_merge(const MergeArgs& a, int32_t d, hipStream_t stream, const char** name);
 hipError_t launch_tq_encode(const TqArgs& a, int32_t d, int32_t bits, int32_t x_dtype, hipStream_t stream,
                             const char** name);
