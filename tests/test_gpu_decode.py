@@ -99,7 +99,9 @@ def test_decode_split_count_independence_and_determinism():
 
 
 def test_decode_extreme_scales():
-    """Per-token scales spanning many octaves within one head (outlier tokens)."""
+    """Per-token scales spanning many octaves within one head (outlier tokens).  The outputs reach
+    about 1e3, where fp32 itself resolves only about 1e-4, so the bar is applied relative to the
+    largest output; the absolute bar is exercised at unit scale by the other decode tests."""
     import int8_compressed_kv_amd as fa
     torch_gpu()
     q, k, v = rng_normal(604, (4, 1, 128), (1, 4000, 128), (1, 4000, 128))
