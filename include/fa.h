@@ -20,7 +20,7 @@
  *                      prefill exchanges (kernbench2 ADR-0060 commit: partial (m, l, O)
  *                      states reduced into one).
  *   fa_tq_codebook, fa_tq_encode, fa_tq_decode
- *                   -- the TurboQuant 2/4-bit KV codec: randomized Hadamard rotation,
+ *                   -- the TurboQuant 2-4-bit KV codec: randomized Hadamard rotation,
  *                      L2 normalisation, Lloyd-Max codebook of the Beta(d/2, d/2)
  *                      coordinate law, bit-packing (Foundry attention/ README, section
  *                      "TurboQuant KV Cache Compression").
@@ -166,7 +166,7 @@ int fa_merge_lse(const float* o_parts, const float* lse_parts, int32_t n_parts, 
  * `centroids`) of u = 2B - 1 with B ~ Beta(head_dim/2, head_dim/2), the coordinate law the
  * TurboQuant page quantizes against (Foundry attention/ README, TurboQuant section).  Computed
  * on the host (Lloyd-Max iterations, Gauss-Legendre quadrature), about 0.1 s; callers keep it.
- * head_dim in {32, 64, 128, 256}, bits in {2, 4}.
+ * head_dim in {32, 64, 128, 256}, bits in {2, 3, 4}.
  */
 int fa_tq_codebook(int32_t head_dim, int32_t bits, float* centroids);
 
@@ -197,6 +197,41 @@ int fa_tq_encode(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t head_
  */
 int fa_tq_decode(const uint8_t* codes, const float* norms, int64_t n_tokens, int32_t head_dim, int32_t bits,
                  const int8_t* signs, const float* codebook, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * fa_tq_attention_decode -- one decode step (as fa_decode) over a KV cache held as TurboQuant
+ * codes, read directly: the codes are turned into matrix-core operands in registers and the
+ * decoded cache is never written to memory (Foundry attention/ README, section "TurboQuant KV
+ * Cache Compression": K and V stored as rotated, normalised Lloyd-Max codes; fkl PR, Summary:
+ * the compressed cache is dequantized inside q.k and p.v).  The result is attention over
+ *   K^_j = k_signs * H (k_norms_j k_codebook[code_j]) / sqrt(d), V^_j likewise,
+ * the vectors fa_tq_decode would produce: scores use q' = H (k_signs * q) against the codebook,
+ * P.V is accumulated in the rotated domain and rotated back once per head.
+ *   q          device [bh_q, 1, head_dim], FA_BF16 or FA_F32.
+ *   k_codes    device uint8 [bh_kv, s_k, head_dim k_bits / 8] as fa_tq_encode writes them;
+ *              k_norms device fp32 [bh_kv, s_k]; k_signs device int8 [head_dim]; k_codebook host
+ *              fp32 [2^k_bits], strictly increasing; likewise for V.
+ *   k_bits, v_bits  2 or 4.  head_dim 64 or 128.
+ *   out, lse_out, softmax_scale, window, num_splits, epi, workspace: as for fa_decode, with
+ *              fa_tq_attention_num_splits / fa_tq_attention_workspace_bytes for the sizes.
+ * The codebooks enter as three 7-bit digits each (2^-22 of their largest entry); all other
+ * arithmetic is exact in integers or fp32.
+ */
+int fa_tq_attention_decode(const void* q, int32_t q_dtype,
+                           const uint8_t* k_codes, const float* k_norms, const int8_t* k_signs, int32_t k_bits,
+                           const float* k_codebook,
+                           const uint8_t* v_codes, const float* v_norms, const int8_t* v_signs, int32_t v_bits,
+                           const float* v_codebook,
+                           void* out, int32_t out_dtype, float* lse_out,
+                           int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim,
+                           float softmax_scale, int32_t window, int32_t num_splits,
+                           const fa_epilogue_op* epi, int32_t n_epi,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count and workspace bytes of fa_tq_attention_decode (num_splits 0 = automatic). */
+int32_t fa_tq_attention_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim);
+size_t fa_tq_attention_workspace_bytes(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim,
+                                       int32_t num_splits);
 
 /*
  * fa_decode_num_splits -- the split count fa_decode uses when num_splits == 0.

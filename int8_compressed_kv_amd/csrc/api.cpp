@@ -71,6 +71,32 @@ float resolve_scale(float s, int32_t d) {
 
 constexpr int32_t kMaxSplits = 4096;
 constexpr int32_t kDecodeTile = 32;   // keys per decode tile
+constexpr int32_t kTqAttnTile = 64;   // keys per TurboQuant attention tile
+
+// The codebook c[0 .. 2^bits) as three signed 7-bit digits of c 2^-E (|c| 2^-E < 1/2):
+// c ~ 2^E (d0 / 2^7 + d1 / 2^14 + d2 / 2^21), each digit the nearest integer to what remains;
+// byte k of tab[t] holds digit t of entry k.  Returns E.
+int codebook_digits(const float* cb, int32_t bits, uint32_t (*tab)[4]) {
+  const int n = 1 << bits;
+  double mx = 0.0;
+  for (int k = 0; k < n; ++k) mx = std::fmax(mx, std::fabs((double)cb[k]));
+  int E = 0;
+  if (mx > 0.0) {
+    (void)std::frexp(mx, &E);
+    E += 1;
+  }
+  for (int t = 0; t < 3; ++t)
+    for (int w = 0; w < 4; ++w) tab[t][w] = 0u;
+  for (int k = 0; k < n; ++k) {
+    double x = std::ldexp((double)cb[k], -E) * 128.0;
+    for (int t = 0; t < 3; ++t) {
+      const double dd = std::nearbyint(x);
+      x = (x - dd) * 128.0;
+      tab[t][k / 4] |= ((uint32_t)(int32_t)dd & 0xffu) << (8 * (k % 4));
+    }
+  }
+  return E;
+}
 
 }  // namespace
 
@@ -237,7 +263,7 @@ namespace {
 int check_tq(int32_t head_dim, int32_t bits) {
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(FA_ERR_UNSUPPORTED, "TurboQuant needs a power-of-two head_dim in [32, 256] (got %d)", head_dim);
-  if (bits != 2 && bits != 4) return fail(FA_ERR_UNSUPPORTED, "TurboQuant bits must be 2 or 4 (got %d)", bits);
+  if (bits < 2 || bits > 4) return fail(FA_ERR_UNSUPPORTED, "TurboQuant bits must be 2, 3 or 4 (got %d)", bits);
   return FA_OK;
 }
 int check_codebook(const float* cb, int32_t bits) {
@@ -436,5 +462,98 @@ int fa_decode_noalloc(const void* q, int32_t q_dtype, const int8_t* k, const int
 }
 
 size_t fa_decode_noalloc_max_bytes(void) { return fa::kDecodeScratchBytes; }
+
+int32_t fa_tq_attention_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim) {
+  (void)head_dim;
+  if (bh_kv <= 0 || bh_q <= 0 || s_k <= 0) return 1;
+  const int32_t group = bh_q / bh_kv;
+  const int64_t units = (int64_t)bh_kv * ((group + 3) / 4);
+  const int32_t tiles = (s_k + kTqAttnTile - 1) / kTqAttnTile;
+  // one workgroup per CU (256), each split keeping at least 8 tiles (2 per wave)
+  int64_t splits = (256 + units - 1) / units;
+  const int64_t max_by_len = tiles / 8 > 0 ? tiles / 8 : 1;
+  if (splits > max_by_len) splits = max_by_len;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits < 1) splits = 1;
+  return (int32_t)splits;
+}
+
+size_t fa_tq_attention_workspace_bytes(int32_t bh_q, int32_t bh_kv, int32_t s_k, int32_t head_dim,
+                                       int32_t num_splits) {
+  if (bh_q <= 0 || head_dim <= 0) return 0;
+  if (num_splits <= 0) num_splits = fa_tq_attention_num_splits(bh_q, bh_kv, s_k, head_dim);
+  return (size_t)bh_q * (size_t)num_splits * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+int fa_tq_attention_decode(const void* q, int32_t q_dtype, const uint8_t* k_codes, const float* k_norms,
+                           const int8_t* k_signs, int32_t k_bits, const float* k_codebook, const uint8_t* v_codes,
+                           const float* v_norms, const int8_t* v_signs, int32_t v_bits, const float* v_codebook,
+                           void* out, int32_t out_dtype, float* lse_out, int32_t bh_q, int32_t bh_kv, int32_t s_k,
+                           int32_t head_dim, float softmax_scale, int32_t window, int32_t num_splits,
+                           const fa_epilogue_op* epi, int32_t n_epi, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_last_error.clear();
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "TurboQuant attention needs head_dim 64 or 128 (got %d)", head_dim);
+  if ((k_bits != 2 && k_bits != 4) || (v_bits != 2 && v_bits != 4))
+    return fail(FA_ERR_UNSUPPORTED, "TurboQuant attention reads 2- or 4-bit codes (got K %d, V %d)", k_bits, v_bits);
+  if (bh_q <= 0 || bh_kv <= 0) return fail(FA_ERR_INVALID, "bh_q and bh_kv must be positive");
+  if (bh_q % bh_kv != 0) return fail(FA_ERR_INVALID, "bh_q (%d) must be a multiple of bh_kv (%d)", bh_q, bh_kv);
+  if (s_k < 0) return fail(FA_ERR_INVALID, "s_k must be >= 0");
+  if (window < 0) return fail(FA_ERR_INVALID, "window must be >= 0");
+  if (q_dtype != FA_F32 && q_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "q must be FA_F32 or FA_BF16");
+  if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "out must be FA_F32 or FA_BF16");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(FA_ERR_INVALID, "num_splits must be in [0, %d] (got %d)", kMaxSplits, num_splits);
+  if (int r = check_codebook(k_codebook, k_bits)) return r;
+  if (int r = check_codebook(v_codebook, v_bits)) return r;
+  fa::EpiArgs ea;
+  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  if (!q || !out || !k_signs || !v_signs) return fail(FA_ERR_INVALID, "null q, out or signs");
+  if (s_k > 0 && (!k_codes || !v_codes || !k_norms || !v_norms)) return fail(FA_ERR_INVALID, "null codes or norms");
+  if (!aligned16(q) || !aligned16(out) || (s_k > 0 && (!aligned16(k_codes) || !aligned16(v_codes))))
+    return fail(FA_ERR_INVALID, "q, codes and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(k_norms) & 3u) || (reinterpret_cast<uintptr_t>(v_norms) & 3u) ||
+      (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)))
+    return fail(FA_ERR_INVALID, "norms and lse_out must be 4-byte aligned");
+  const int32_t splits = num_splits > 0 ? num_splits : fa_tq_attention_num_splits(bh_q, bh_kv, s_k, head_dim);
+  const size_t need = (size_t)bh_q * (size_t)splits * (size_t)(head_dim + 2) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "TurboQuant attention workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID, "workspace must be 16-byte aligned");
+
+  fa::TqAttnArgs a{};
+  a.q = q;
+  a.kc = k_codes;
+  a.kn = k_norms;
+  a.vc = v_codes;
+  a.vn = v_norms;
+  a.ks = k_signs;
+  a.vs = v_signs;
+  a.out = out;
+  a.lse = lse_out;
+  a.partial = static_cast<float*>(workspace);
+  a.bh_q = bh_q;
+  a.bh_kv = bh_kv;
+  a.group = bh_q / bh_kv;
+  a.s_k = s_k;
+  a.key_lo = (window > 0 && window < s_k) ? s_k - window : 0;
+  a.num_splits = splits;
+  const int32_t tiles = (s_k - a.key_lo + kTqAttnTile - 1) / kTqAttnTile;
+  a.tiles_per_split = (tiles + splits - 1) / splits;
+  a.q_bf16 = q_dtype == FA_BF16;
+  a.out_bf16 = out_dtype == FA_BF16;
+  a.scale = resolve_scale(softmax_scale, head_dim);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.k_e = codebook_digits(k_codebook, k_bits, a.ktab);
+  a.v_e = codebook_digits(v_codebook, v_bits, a.vtab);
+  a.epi = ea;
+  const char* name = "";
+  hipError_t e = fa::launch_tq_attention(a, head_dim, k_bits, v_bits, static_cast<hipStream_t>(stream), &name);
+  if (e != hipSuccess) return hip_fail(e, "TurboQuant attention launch");
+  g_last_kernel = name;
+  return FA_OK;
+}
 
 }  // extern "C"

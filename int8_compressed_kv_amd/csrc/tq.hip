@@ -1,4 +1,4 @@
-// TurboQuant KV codec: 2- or 4-bit codes per channel from a randomized Hadamard rotation, an
+// TurboQuant KV codec: 2-, 3- or 4-bit codes per channel from a randomized Hadamard rotation, an
 // L2 normalisation and a Lloyd-Max scalar codebook (Foundry attention/ README, section
 // "TurboQuant KV Cache Compression": signs applied before the Hadamard transform, the L2 norm
 // as normaliser, Lloyd-Max quantization against Beta(d/2, d/2) codebooks, bit-packing).
@@ -6,12 +6,14 @@
 // Per vector x (head_dim d, a power of two) with random signs s:
 //   y = H (s * x) (Sylvester Hadamard, unnormalised), n = ||x||, u = y / ||y||,
 //   code_i = number of thresholds t_k <= u_i (thresholds = midpoints of the codebook),
-//   packed little-endian, channel i at bit (i b) mod 8 of byte (i b) / 8; n stored as fp32.
+//   packed as one little-endian bit stream per vector, channel i at stream bits i b .. i b + b - 1
+//   (a 3-bit code may straddle two bytes); n stored as fp32.
 // Decode: x_hat = s * H (n c[code]) / sqrt(d).
 //
 // A segment of d / 16 lanes owns a vector, 16 values per lane; only the Hadamard stages over
 // the lane bits of a channel index cross lanes (DPP quad permutes and ds_swizzle).  Decisions use
-// the codebook's antisymmetry (a 3-step binary search over the positive thresholds at 4 bits).
+// the codebook's antisymmetry (a binary search over the positive thresholds: 2 steps at 3 bits,
+// 3 at 4 bits, or a bucket table at 4 bits).
 // The codebook itself is computed on the host (fa_tq_codebook): Lloyd-Max iterations with the
 // cell masses and first moments of the Beta(d/2, d/2) law integrated by Gauss-Legendre
 // quadrature.
@@ -25,8 +27,9 @@ namespace fa {
 namespace {
 
 // A segment of SEG = d/16 lanes owns a vector, 16 values per lane: lane sl holds channels
-// 16 sl .. 16 sl + 15 (NCH chunks of CE values, 16 bytes each), so its codes are one contiguous
-// 8- or 4-byte word and its loads and stores contiguous runs.  Channel c = 16 sl + CE j + e: the
+// 16 sl .. 16 sl + 15 (NCH chunks of CE values, 16 bytes each), so its codes are 2 BITS contiguous
+// bytes (one 8- or 4-byte word at 4 or 2 bits, three 2-byte words at 3 bits) and its loads and
+// stores contiguous runs.  Channel c = 16 sl + CE j + e: the
 // Hadamard stages over
 // the bits of e and j stay inside the lane, the stages over the bits of sl cross lanes.
 template <int CE>
@@ -109,7 +112,8 @@ __device__ __forceinline__ void channel_factors(float (&f)[16], const int8_t* si
 // t[h - 1] = 0 and positive thresholds tp[m] = t[h + m], h = 2^(bits-1)): u >= 0 gives
 // h + #{tp <= u}; u < 0 gives (h - 1) - #{tp < |u|}, and #{tp < |u|} is the <= count at the
 // float just below |u|.  With m = -1 for u < 0 (0 otherwise) both are (count ^ m) + h.  u must
-// not be -0.  At 4 bits the count over the 7 positive thresholds is a 3-step binary search.
+// not be -0.  The count over the h - 1 positive thresholds is a binary search: 2 steps over 3
+// thresholds at 3 bits, 3 steps over 7 at 4 bits.
 template <int BITS>
 __device__ __forceinline__ unsigned tq_code(float u, const float (&tp)[7]) {
   constexpr int H = 1 << (BITS - 1);
@@ -119,6 +123,9 @@ __device__ __forceinline__ unsigned tq_code(float u, const float (&tp)[7]) {
   int cnt;
   if constexpr (BITS == 2) {
     cnt = x >= tp[0] ? 1 : 0;
+  } else if constexpr (BITS == 3) {
+    const bool c0 = x >= tp[1];
+    cnt = (c0 ? 2 : 0) + (x >= (c0 ? tp[2] : tp[0]) ? 1 : 0);
   } else {
     const bool c0 = x >= tp[3];
     const float t1 = c0 ? tp[5] : tp[1];
@@ -232,17 +239,23 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
     const float ny = __fsqrt_rn(segment_sum<SEG>(yy));
     const float inv = ny > 0.f ? __fdiv_rn(1.0f, ny) : 0.f;
     if (row < a.n) {
-      // the lane's 16 codes, channel 16 sl + i at bit BITS i of a little-endian word
-      unsigned packed[BITS / 2] = {};
+      // the lane's 16 codes, channel 16 sl + i at bit BITS i of a little-endian word of 16 BITS bits
+      uint64_t packed = 0;
       // fma with +0 rounds like the product and turns a -0 product into +0
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        packed[(BITS * i) / 32] |= (TABLE ? tq_code4_tab(__builtin_fmaf(v[i], inv, 0.0f), tab)
-                                          : tq_code<BITS>(__builtin_fmaf(v[i], inv, 0.0f), tp))
-                                   << ((BITS * i) % 32);
+        packed |= (uint64_t)(TABLE ? tq_code4_tab(__builtin_fmaf(v[i], inv, 0.0f), tab)
+                                   : tq_code<BITS>(__builtin_fmaf(v[i], inv, 0.0f), tp))
+                  << (BITS * i);
       uint8_t* dst = a.codes + row * (D * BITS / 8) + sl * (2 * BITS);
-      if constexpr (BITS == 4) *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
-      else *reinterpret_cast<unsigned*>(dst) = packed[0];
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{(unsigned)packed, (unsigned)(packed >> 32)};
+      } else if constexpr (BITS == 3) {   // 6 bytes at an even offset
+#pragma unroll
+        for (int h = 0; h < 3; ++h) reinterpret_cast<unsigned short*>(dst)[h] = (unsigned short)(packed >> (16 * h));
+      } else {
+        *reinterpret_cast<unsigned*>(dst) = (unsigned)packed;
+      }
       if (sl == 0) a.norms[row] = n;
     }
     if (it + 1 < kTqEncIter) {
@@ -257,7 +270,6 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   constexpr int CE = 4;                       // fp32 values per chunk of the layout
   constexpr int SEG = D / 16;
   constexpr int RPW = 64 / SEG;
-  constexpr int NW = BITS / 2;                // 32-bit words of a lane's 16 codes
   __shared__ float cb[16];
   if (threadIdx.x < 16) cb[threadIdx.x] = a.cb[threadIdx.x];
   const int lane = threadIdx.x & 63;
@@ -265,19 +277,21 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqDecIter;
   // all row groups' codes (the lane's contiguous 16) and norms are loaded up front (rows past the
   // end repeat the last row)
-  unsigned pk[kTqDecIter][NW];
+  uint64_t pk[kTqDecIter];   // the lane's 16 codes, channel 16 sl + i at bit BITS i
   float nn[kTqDecIter];
 #pragma unroll
   for (int it = 0; it < kTqDecIter; ++it) {
     const int64_t r = min((g0 + it) * RPW + lane / SEG, a.n - 1);
     nn[it] = a.norms[r];
     const uint8_t* src = a.codes + r * (D * BITS / 8) + sl * (2 * BITS);
-    if constexpr (NW == 2) {
+    if constexpr (BITS == 4) {
       const u32x2 w = *reinterpret_cast<const u32x2*>(src);
-      pk[it][0] = w[0];
-      pk[it][NW - 1] = w[1];
+      pk[it] = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+    } else if constexpr (BITS == 3) {
+      const unsigned short* s16 = reinterpret_cast<const unsigned short*>(src);
+      pk[it] = (uint64_t)s16[0] | ((uint64_t)s16[1] << 16) | ((uint64_t)s16[2] << 32);
     } else {
-      pk[it][0] = *reinterpret_cast<const unsigned*>(src);
+      pk[it] = *reinterpret_cast<const unsigned*>(src);
     }
   }
   float f[16];
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
     // rounded on its own: an fma with the first butterfly's add would round differently
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      v[i] = mul_rn(nn[it], cb[(pk[it][(BITS * i) / 32] >> ((BITS * i) % 32)) & ((1u << BITS) - 1)]);
+      v[i] = mul_rn(nn[it], cb[(unsigned)(pk[it] >> (BITS * i)) & ((1u << BITS) - 1)]);
     hadamard16<CE, SEG>(v, sl);
     if (row < a.n) {
       float y[16];
@@ -457,12 +471,16 @@ int tq_codebook(int32_t d, int32_t bits, float* centroids) {
 hipError_t launch_tq_encode(const TqArgs& a, int32_t d, int32_t bits, int32_t x_dtype, hipStream_t st,
                             const char** name) {
   const bool bf16 = x_dtype == kBF16;
-  return bits == 4 ? encode_bits<4>(a, d, bf16, st, name) : encode_bits<2>(a, d, bf16, st, name);
+  if (bits == 4) return encode_bits<4>(a, d, bf16, st, name);
+  if (bits == 3) return encode_bits<3>(a, d, bf16, st, name);
+  return encode_bits<2>(a, d, bf16, st, name);
 }
 
 hipError_t launch_tq_decode(const TqArgs& a, int32_t d, int32_t bits, bool bf16_out, hipStream_t st,
                             const char** name) {
-  return bits == 4 ? decode_bits<4>(a, d, bf16_out, st, name) : decode_bits<2>(a, d, bf16_out, st, name);
+  if (bits == 4) return decode_bits<4>(a, d, bf16_out, st, name);
+  if (bits == 3) return decode_bits<3>(a, d, bf16_out, st, name);
+  return decode_bits<2>(a, d, bf16_out, st, name);
 }
 
 }  // namespace fa

@@ -13,13 +13,15 @@ Modules
   quantize   -- the per-token absmax/127 int8 quantizer (numpy fp32), the
                 closed-form compression ratio and the decode-time cache write.
   turboquant -- the 2-4-bit TurboQuant codec: randomized Hadamard rotation, L2
-                normalisation, Lloyd-Max codebooks for Beta(d/2, d/2), packing.
+                normalisation, Lloyd-Max codebooks for Beta(d/2, d/2), packing, and
+                decode attention over a cache held as such codes.
 
-Every function is pinned by tests in tests/test_oracle_pins.py (brute force,
-a library cross-check, invariants and closed forms).  No function here is
+Every function is pinned by tests in tests/test_oracle_pins.py and
+tests/test_oracle_turboquant.py (brute force, a library cross-check, invariants
+and closed forms).  No function here is
 "parity unpinned".
 """
 from .attention import attention, apply_epilogue, dequantize, visible_mask, decode, merge_lse  # noqa: F401
 from .quantize import quantize_per_token, compression_ratio, append_kv  # noqa: F401
 from .turboquant import (hadamard, beta_codebook, tq_encode, tq_decode, tq_pack, tq_unpack,  # noqa: F401
-                         tq_compression_ratio)
+                         tq_compression_ratio, tq_attention_decode)

@@ -20,8 +20,10 @@ Readings where the page is silent (its spec is not on the pages):
   centroids (iterated to convergence).  A coordinate exactly on a threshold takes
   the upper cell.
 * Decode: x_hat = s * H (n * c[code]) / sqrt(d) (no renormalisation).
-* Packing: channel i's b-bit code sits at bit (i b) mod 8 of byte (i b) // 8,
-  little-endian; b in {2, 4} (the K4/V2 and K4/V4 configurations the page quotes).
+* Packing: the codes of a vector form one little-endian bit stream, channel i's
+  b-bit code at bits i b .. i b + b - 1 (bit k of the stream is bit k mod 8 of
+  byte k // 8); b in {2, 3, 4}, the page's "2-4 bits per channel" (a 3-bit code
+  may straddle two bytes).
 * An all-zero vector has n = 0 and decodes to 0 whatever its codes.
 """
 from __future__ import annotations
@@ -30,7 +32,7 @@ import numpy as np
 from scipy import special
 
 __all__ = ["hadamard", "beta_codebook", "tq_encode", "tq_decode", "tq_pack", "tq_unpack",
-           "tq_compression_ratio"]
+           "tq_compression_ratio", "tq_attention_decode"]
 
 
 def hadamard(d: int) -> np.ndarray:
@@ -97,24 +99,43 @@ def tq_decode(codes, norms, signs, bits: int, codebook=None):
 
 
 def tq_pack(codes, bits: int) -> np.ndarray:
-    """Pack b-bit codes (..., d) into (..., d b / 8) bytes, channel i at bit (i b) mod 8."""
+    """Pack b-bit codes (..., d) into (..., d b / 8) bytes: one little-endian bit stream per
+    vector, channel i's code at stream bits i b .. i b + b - 1."""
     codes = np.asarray(codes, dtype=np.uint8)
-    per = 8 // bits
-    g = codes.reshape(codes.shape[:-1] + (codes.shape[-1] // per, per)).astype(np.uint32)
-    out = np.zeros(g.shape[:-1], np.uint32)
-    for j in range(per):
-        out |= g[..., j] << (bits * j)
-    return out.astype(np.uint8)
+    d = codes.shape[-1]
+    if (d * bits) % 8:
+        raise ValueError("d * bits must be a whole number of bytes")
+    planes = (codes[..., None] >> np.arange(bits, dtype=np.uint8)) & 1        # (..., d, bits), LSB first
+    stream = planes.reshape(codes.shape[:-1] + (d * bits,))
+    return np.packbits(stream, axis=-1, bitorder="little")
 
 
 def tq_unpack(packed, bits: int, d: int) -> np.ndarray:
+    """Inverse of tq_pack: (..., d b / 8) bytes -> (..., d) codes."""
     packed = np.asarray(packed, dtype=np.uint8)
-    per = 8 // bits
-    mask = (1 << bits) - 1
-    parts = [(packed >> (bits * j)) & mask for j in range(per)]
-    return np.stack(parts, axis=-1).reshape(packed.shape[:-1] + (d,)).astype(np.uint8)
+    stream = np.unpackbits(packed, axis=-1, bitorder="little")[..., :d * bits]
+    planes = stream.reshape(packed.shape[:-1] + (d, bits)).astype(np.uint8)
+    return (planes << np.arange(bits, dtype=np.uint8)).sum(axis=-1).astype(np.uint8)
 
 
 def tq_compression_ratio(d: int, k_bits: int, v_bits: int) -> float:
     """fp32 K + V bytes of a token over its packed codes plus one fp32 norm each."""
     return (2 * 4 * d) / (d * k_bits / 8 + d * v_bits / 8 + 8)
+
+
+def tq_attention_decode(q, k_packed, k_norms, k_signs, k_bits: int, v_packed, v_norms, v_signs, v_bits: int, *,
+                        k_codebook=None, v_codebook=None, window: int = 0, scale=None, epilogue=()):
+    """Decode attention over a KV cache held as TurboQuant codes: the plain definition, i.e. the
+    vectors tq_decode reconstructs from the packed codes and norms, attended by the fp64 decode
+    (Foundry attention/ README, TurboQuant section: the coded cache stands in for K and V).
+    q (bh_q, 1, d); packed codes (bh_kv, s_k, d bits / 8); norms (bh_kv, s_k); codebooks are the
+    centroid arrays (default: beta_codebook).  Returns (out, lse) as oracle.decode does."""
+    from .attention import decode
+    kp = np.asarray(k_packed)
+    vp = np.asarray(v_packed)
+    d = np.asarray(q).shape[-1]
+    kcb = None if k_codebook is None else (np.asarray(k_codebook, np.float64), None)
+    vcb = None if v_codebook is None else (np.asarray(v_codebook, np.float64), None)
+    kh = tq_decode(tq_unpack(kp, k_bits, d), k_norms, k_signs, k_bits, kcb)
+    vh = tq_decode(tq_unpack(vp, v_bits, d), v_norms, v_signs, v_bits, vcb)
+    return decode(q, kh, vh, window=window, scale=scale, epilogue=epilogue)

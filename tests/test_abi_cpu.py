@@ -206,13 +206,13 @@ def test_tq_codebook_on_host_matches_the_oracle_in_fp32(L):
     import numpy as np
     import oracle
     for d in (32, 64, 128, 256):
-        for bits in (2, 4):
+        for bits in (2, 3, 4):
             cb = fa.tq_codebook(d, bits)
             ref, _ = oracle.beta_codebook(d, bits)
             assert np.abs(cb.astype(np.float64) - ref).max() < 1e-7 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("d,bits,code", [(96, 4, -2), (64, 3, -2), (512, 2, -2)])
+@pytest.mark.parametrize("d,bits,code", [(96, 4, -2), (64, 5, -2), (64, 1, -2), (512, 2, -2)])
 def test_tq_rejects_unsupported_shapes(L, d, bits, code):
     import numpy as np
     out = np.zeros(16, np.float32)
@@ -233,7 +233,7 @@ def test_tq_rejects_bad_codebook_and_pointers(L):
     assert L.fa_tq_encode(vp(1 << 20), 0, 4, 64, 2, vp(1 << 20), vp(shifted.ctypes.data), vp(1 << 20), vp(1 << 20), None) == -1
     assert "antisymmetric" in fa.last_error()
     for d in (32, 64, 128, 256):
-        for bits in (2, 4):
+        for bits in (2, 3, 4):
             cb = fa.tq_codebook(d, bits)
             assert np.array_equal(cb, -cb[::-1]), "the host codebook is not exactly antisymmetric"
     assert L.fa_tq_encode(vp(0), 0, 0, 64, 2, vp(0), vp(good.ctypes.data), vp(0), vp(0), None) == 0

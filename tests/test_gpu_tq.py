@@ -1,4 +1,4 @@
-"""GPU parity of the TurboQuant codec against the oracle: codes equal except where the exact
+"""GPU parity of the TurboQuant codec (2, 3 and 4 bits) against the oracle: codes equal except where the exact
 rotated coordinate lies on a decision threshold (there either neighbouring code is correct),
 norms and decoded vectors to fp32 rounding, and attention over a K4/V2 and a K4/V4 cache with the
 quality the page quotes."""
@@ -26,7 +26,7 @@ def _encode(x, xdt, bits, signs):
 
 
 @pytest.mark.parametrize("d", [32, 64, 128, 256])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("xdt", ["f32", "bf16"])
 def test_encode_matches_oracle_up_to_threshold_ties(d, bits, xdt):
     torch_gpu()
@@ -86,7 +86,7 @@ def test_encode_with_codebooks_outside_the_decision_table(which):
     assert fa.last_kernel() == "tq_encode"
 
 
-@pytest.mark.parametrize("d,bits", [(64, 2), (128, 4), (256, 4), (32, 2)])
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 4), (256, 4), (32, 2), (32, 3), (64, 3), (128, 3), (256, 3)])
 def test_decode_matches_oracle_on_the_same_codes(d, bits):
     import int8_compressed_kv_amd as fa
     torch = torch_gpu()

@@ -81,7 +81,7 @@ def test_basis_vector_encodes_to_one_repeated_code_by_hand():
 def test_zero_vector_and_packing_round_trip():
     d = 128
     s = random_signs(8, d)
-    for bits in (2, 4):
+    for bits in (2, 3, 4):
         codes, n = oracle.tq_encode(np.zeros((3, d)), s, bits)
         assert np.all(n == 0) and np.all(oracle.tq_decode(codes, n, s, bits) == 0)
         g = np.random.Generator(np.random.PCG64(bits))
@@ -92,6 +92,27 @@ def test_zero_vector_and_packing_round_trip():
     # bit layout by hand: codes 1, 2, 3, 0 at 2 bits -> 0b00111001; 0xA, 0x5 at 4 bits -> 0x5A
     assert oracle.tq_pack(np.array([[1, 2, 3, 0]], np.uint8), 2)[0, 0] == 0b00111001
     assert oracle.tq_pack(np.array([[0xA, 0x5]], np.uint8), 4)[0, 0] == 0x5A
+
+
+def test_three_bit_packing_against_a_hand_packed_stream():
+    """3-bit codes straddle bytes: the packed stream of a hand-worked example, and the same rule
+    checked bit by bit against a plain loop over the stream positions."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tq_pack3_hand.json")))
+    pk = oracle.tq_pack(np.array([g["codes"]], np.uint8), g["bits"])
+    assert pk[0].tolist() == g["bytes"]
+    assert oracle.tq_unpack(pk, 3, 8)[0].tolist() == g["codes"]
+    rng = np.random.Generator(np.random.PCG64(33))
+    cc = rng.integers(0, 8, (4, 64)).astype(np.uint8)
+    pk = oracle.tq_pack(cc, 3)
+    for r in range(4):
+        for i in range(64):
+            got = 0
+            for b in range(3):
+                k = 3 * i + b
+                got |= ((int(pk[r, k // 8]) >> (k % 8)) & 1) << b
+            assert got == cc[r, i]
 
 
 def test_k4v2_size_ratio_matches_printed_value():
@@ -119,3 +140,42 @@ def test_attention_quality_magnitudes_like_the_page():
     c42, c44 = cos(4, 2), cos(4, 4)
     assert abs(c42 - gv["k4v2_synthetic"]) < 0.03, c42
     assert c44 > gv["k4v4"] - 0.01 and c44 > c42, c44
+
+
+def test_attention_over_codes_by_brute_force():
+    """Decode attention over TurboQuant codes, pinned by pure-Python loops that rebuild every key
+    and value from its codes by the page's steps (centroid times norm, Hadamard entries
+    (-1)^popcount(i & j), signs, 1/sqrt(d)) and take the softmax with math.exp / math.fsum."""
+    import math
+    d, s_k, G = 8, 5, 2
+    rng = np.random.Generator(np.random.PCG64(77))
+    q = rng.standard_normal((2 * G, 1, d))
+    k = rng.standard_normal((2, s_k, d))
+    v = rng.standard_normal((2, s_k, d)) + 0.5
+    sk = np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+    sv = np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+    for kb, vb in ((4, 2), (3, 4)):
+        kc, kn = oracle.tq_encode(k, sk, kb)
+        vc, vn = oracle.tq_encode(v, sv, vb)
+        ccb_k, _ = oracle.beta_codebook(d, kb)
+        ccb_v, _ = oracle.beta_codebook(d, vb)
+        out, lse = oracle.tq_attention_decode(q, oracle.tq_pack(kc, kb), kn, sk, kb, oracle.tq_pack(vc, vb), vn,
+                                              sv, vb, window=4)
+
+        def rebuild(codes, norm, signs, cb):
+            y = [float(norm) * float(cb[c]) for c in codes]
+            return [signs[i] * math.fsum((-1) ** bin(i & j).count("1") * y[j] for j in range(d)) / math.sqrt(d)
+                    for i in range(d)]
+        for h in range(2 * G):
+            b = h // G
+            keys = range(s_k - 4, s_k)                     # window 4 keeps the last four keys
+            kk = {j: rebuild(kc[b, j], kn[b, j], sk, ccb_k) for j in keys}
+            vv = {j: rebuild(vc[b, j], vn[b, j], sv, ccb_v) for j in keys}
+            sc = {j: math.fsum(q[h, 0, i] * kk[j][i] for i in range(d)) / math.sqrt(d) for j in keys}
+            m = max(sc.values())
+            w = {j: math.exp(sc[j] - m) for j in keys}
+            tot = math.fsum(w.values())
+            for i in range(d):
+                ref = math.fsum(w[j] * vv[j][i] for j in keys) / tot
+                assert abs(out[h, 0, i] - ref) < 1e-12
+            assert abs(lse[h, 0] - (m + math.log(tot))) < 1e-12
