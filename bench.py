@@ -13,6 +13,8 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   append decode-time cache write of the c4 shape: one new fp32 K and V token per KV head (128),
          quantized into the 32768-row int8 cache at device-held positions (latency-bound)
   tq     TurboQuant 4-bit encode of the c4 K cache (fp32 in) and decode of it back to bf16
+  tqattn decode attention read straight from TurboQuant codes of the c4 cache (K 4-bit, V 2-bit,
+         the page's default), 16 x 32 query / 8 KV heads, 32768 keys, d 128
   merge  log-sum-exp merge of 8 key-chunk results for one 4096-row query chunk of the c5 shape
          (64 heads x 4096 rows, d 128, fp32 parts, bf16 output): the exchange of a ring prefill
   copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
@@ -64,6 +66,7 @@ LEG_SOURCES = {
     "merge": ("merge.hip", "device_common.hpp", "kernel_args.hpp"),
     "tq": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
     "tq_dec": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
+    "tqattn": ("tq_attn.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
@@ -164,7 +167,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="c5,c5w,c3,c4,c4g8,comp,append,merge,tq")
+    ap.add_argument("--legs", default="c5,c5w,c3,c4,c4g8,comp,append,merge,tq,tqattn")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
     args = ap.parse_args()
@@ -242,7 +245,7 @@ def main():
         del qd, kc, ks, vc, vs, out, q, k, v
 
     # ------------------------------------------------------------------ compress + decode c4
-    if legs & {"c4", "c4g8", "comp", "append", "tq"}:
+    if legs & {"c4", "c4g8", "comp", "append", "tq", "tqattn"}:
         w = WORKLOADS["c4"]
         log(f"[bench] generating {w.name}")
         q, k, v = draw_qkv(w)
@@ -290,6 +293,30 @@ def main():
                              "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] tq decode: {avg:.3f} ms  {res['tq_dec']['gbs']:.0f} GB/s")
             del codes, norms, kb16, signs
+        if "tqattn" in legs:
+            from synth_inputs import random_signs
+            kbits, vbits = 4, 2
+            kcb, vcb = fa.tq_codebook(w.d, kbits), fa.tq_codebook(w.d, vbits)
+            sk = torch.from_numpy(random_signs(64, w.d)).cuda()
+            sv = torch.from_numpy(random_signs(65, w.d)).cuda()
+            kcode, kn = fa.tq_encode(kf, sk, kbits, kcb)
+            vcode, vn = fa.tq_encode(vf, sv, vbits, vcb)
+            out_t = torch.empty((w.bh_q, 1, w.d), dtype=torch.float32, device="cuda")
+            splits_t = int(fa.lib().fa_tq_attention_num_splits(w.bh_q, w.bh_kv, w.s_k, w.d))
+            ws_t = torch.empty(int(fa.lib().fa_tq_attention_workspace_bytes(w.bh_q, w.bh_kv, w.s_k, w.d, splits_t)),
+                               dtype=torch.uint8, device="cuda")
+            fn = lambda: fa.tq_attention_decode(qd, kcode, kn, sk, kbits, kcb, vcode, vn, sv, vbits, vcb,   # noqa: E731
+                                                num_splits=splits_t, out=out_t, workspace=ws_t)
+            log("[bench] timing decode attention over TurboQuant codes (K4/V2, c4 shape)")
+            ms = timer.run(fn, args.steps, args.warmup, flush=flush)
+            avg = float(np.mean(ms))
+            nbytes = n_tok * (w.d * kbits // 8 + 4 + w.d * vbits // 8 + 4) + w.bh_q * w.d * 2 + w.bh_q * w.d * 4
+            res["tqattn"] = {"workload": "tq_attention_decode_k4v2_b16_h32kv8_sk32768_d128", "ms": avg,
+                             "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "num_splits": splits_t,
+                             "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
+                             "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] tqattn: {avg * 1e3:.1f} us  {res['tqattn']['gbs']:.0f} GB/s")
+            del kcode, kn, vcode, vn, out_t, ws_t, sk, sv
         fa.compress_kv(kf, kc, ks)
         fa.compress_kv(vf, vc, vs)
         if "append" in legs:

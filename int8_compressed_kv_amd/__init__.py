@@ -16,6 +16,7 @@ present, the calls raise.
     cb = tq_codebook(128, 4)                             # TurboQuant: Lloyd-Max codebook (host)
     codes, norms = tq_encode(k, signs, 4, cb)            # 4-bit codes + fp32 norm per token
     k_hat = tq_decode(codes, norms, signs, 4, cb)        # back to fp32 / bf16
+    out = tq_attention_decode(q1, kc, kn, ks, 4, kcb, vc, vn, vs, 2, vcb)   # decode step over codes
 
 Layout (batch*heads, seq, head_dim), head_dim a multiple of 32 up to 256.
 """
@@ -25,7 +26,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Mul", "Add", "Bias", "ReLU", "compress_kv", "append_kv", "tq_codebook", "tq_encode", "tq_decode", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
+__all__ = ["Mul", "Add", "Bias", "ReLU", "compress_kv", "append_kv", "tq_codebook", "tq_encode", "tq_decode", "tq_attention_decode", "flash_attention", "merge_lse", "decode", "decode_workspace_bytes",
            "decode_num_splits", "decode_noalloc", "last_kernel", "last_error", "lib", "LIB_PATH", "FAError",
            "F32", "BF16", "I8"]
 
@@ -105,6 +106,14 @@ def lib() -> ctypes.CDLL:
     L.fa_decode.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32, i32, i32,
                             ctypes.POINTER(_EpiOp), i32, vp, ctypes.c_size_t, vp]
     L.fa_decode.restype = ctypes.c_int
+    L.fa_tq_attention_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp,
+                                         i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(_EpiOp), i32, vp,
+                                         ctypes.c_size_t, vp]
+    L.fa_tq_attention_decode.restype = ctypes.c_int
+    L.fa_tq_attention_num_splits.argtypes = [i32, i32, i32, i32]
+    L.fa_tq_attention_num_splits.restype = i32
+    L.fa_tq_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.fa_tq_attention_workspace_bytes.restype = ctypes.c_size_t
     L.fa_decode_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, f32, i32, i32,
                                     ctypes.POINTER(_EpiOp), i32, vp]
     L.fa_decode_noalloc.restype = ctypes.c_int
@@ -452,3 +461,47 @@ def decode_noalloc(q, k, v, k_scale, v_scale, out, *, lse=None, window=0, scale=
                                    bh_q, bh_kv, s_k, d, float(scale) if scale else 0.0, int(window), int(num_splits),
                                    epi, n_epi, _stream()))
     return out
+
+
+def tq_attention_decode(q, k_codes, k_norms, k_signs, k_bits, k_codebook, v_codes, v_norms, v_signs, v_bits,
+                        v_codebook, *, window=0, scale=None, num_splits=0, epilogue=(), out_dtype=None, out=None,
+                        workspace=None, return_lse=False):
+    """One decode step of q (bh_q, 1, d) over a KV cache held as TurboQuant codes: k_codes
+    (bh_kv, s_k, d k_bits / 8) uint8 with k_norms (bh_kv, s_k) fp32 and k_signs (d,) int8 as
+    tq_encode wrote them, k_codebook the host centroids; likewise for V.  Output fp32 by default."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[1] != 1:
+        raise ValueError("q must have shape (bh_q, 1, head_dim)")
+    bh_q, _, d = q.shape
+    if k_codes.dim() != 3 or v_codes.dim() != 3:
+        raise ValueError("codes must be (bh_kv, s_k, head_dim * bits / 8)")
+    bh_kv, s_k = k_codes.shape[0], k_codes.shape[1]
+    _want(k_codes, "k_codes", (bh_kv, s_k, d * k_bits // 8), torch.uint8)
+    _want(v_codes, "v_codes", (bh_kv, s_k, d * v_bits // 8), torch.uint8)
+    _want(k_norms, "k_norms", (bh_kv, s_k), torch.float32)
+    _want(v_norms, "v_norms", (bh_kv, s_k), torch.float32)
+    _want(k_signs, "k_signs", (d,), torch.int8)
+    _want(v_signs, "v_signs", (d,), torch.int8)
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((bh_q, 1, d), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (bh_q, 1, d):
+        raise ValueError(f"out must have shape {(bh_q, 1, d)}, got {tuple(out.shape)}")
+    _same_device(q, k_codes=k_codes, v_codes=v_codes, k_norms=k_norms, v_norms=v_norms, k_signs=k_signs,
+                 v_signs=v_signs, out=out, workspace=workspace)
+    L = lib()
+    need = int(L.fa_tq_attention_workspace_bytes(bh_q, bh_kv, s_k, d, num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    lse = torch.empty((bh_q,), dtype=torch.float32, device=q.device) if return_lse else None
+    kcb, kcbp = _host_f32(k_codebook)
+    vcb, vcbp = _host_f32(v_codebook)
+    epi, n_epi = _epilogue(epilogue, d)
+    _check(L.fa_tq_attention_decode(_dev(q, "q"), _dtype_code(q), _dev(k_codes, "k_codes"), _dev(k_norms, "k_norms"),
+                                    _dev(k_signs, "k_signs"), int(k_bits), kcbp, _dev(v_codes, "v_codes"),
+                                    _dev(v_norms, "v_norms"), _dev(v_signs, "v_signs"), int(v_bits), vcbp,
+                                    _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"), bh_q, bh_kv, s_k, d,
+                                    float(scale) if scale else 0.0, int(window), int(num_splits), epi, n_epi,
+                                    _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                    _stream()))
+    return (out, lse) if return_lse else out

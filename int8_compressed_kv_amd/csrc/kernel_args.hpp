@@ -92,6 +92,29 @@ struct TqArgs {
   float cb[16];           // decode: the 2^bits centroids, ascending
 };
 
+struct TqAttnArgs {
+  const void* q;          // [bh_q, d] bf16 or fp32
+  const uint8_t* kc;      // K codes [bh_kv, s_k, d kbits / 8]
+  const float* kn;        // K norms [bh_kv, s_k]
+  const uint8_t* vc;      // V codes [bh_kv, s_k, d vbits / 8]
+  const float* vn;        // V norms [bh_kv, s_k]
+  const int8_t* ks;       // K rotation signs [d]
+  const int8_t* vs;       // V rotation signs [d]
+  void* out;              // [bh_q, d]
+  float* lse;             // [bh_q] or null
+  float* partial;         // workspace [bh_q, num_splits, d + 2]: m, l, rotated O
+  int32_t bh_q, bh_kv, group;
+  int32_t s_k, key_lo, num_splits, tiles_per_split;
+  int32_t q_bf16, out_bf16;
+  float scale, scale_log2;
+  // codebooks as three signed 7-bit digits of c[k] 2^-E (c[k] ~ 2^E (d0/2^7 + d1/2^14 + d2/2^21)),
+  // byte k of digit t's 16-byte table; E per codebook
+  uint32_t ktab[3][4];
+  uint32_t vtab[3][4];
+  int32_t k_e, v_e;
+  EpiArgs epi;
+};
+
 // Query heads one decode workgroup serves: 8 (two MFMA column sets) for groups of more than 4
 // heads at head_dim <= 128, else 4.  The split count and the grid both follow it.
 inline int decode_heads_per_workgroup(int group, int head_dim) { return (group > 4 && head_dim <= 128) ? 8 : 4; }
@@ -112,6 +135,8 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t d, hipStream_t stream, con
 // then cached); `device` must be the current device.
 hipError_t decode_scratch_address(int device, void** ptr);
 hipError_t launch_merge(const MergeArgs& a, int32_t d, hipStream_t stream, const char** name);
+hipError_t launch_tq_attention(const TqAttnArgs& a, int32_t d, int32_t kbits, int32_t vbits, hipStream_t stream,
+                               const char** name);
 hipError_t launch_tq_encode(const TqArgs& a, int32_t d, int32_t bits, int32_t x_dtype, hipStream_t stream,
                             const char** name);
 hipError_t launch_tq_decode(const TqArgs& a, int32_t d, int32_t bits, bool bf16_out, hipStream_t stream,

@@ -1,0 +1,599 @@
+// Split-KV decode attention read straight from a TurboQuant-coded KV cache: the codes are turned
+// into MFMA operands in registers and the decoded cache never exists in global memory (Foundry
+// attention/ README, section "TurboQuant KV Cache Compression": K and V stored as randomized
+// Hadamard-rotated, L2-normalised Lloyd-Max codes; fkl.flash_attention PR, Summary: the
+// compressed cache is dequantized inside q.k and p.v).
+//
+// With K^_j = s_K * H (n_j c_K[code_j]) / sqrt(d) (H the symmetric Sylvester Hadamard matrix,
+// s_K the K signs), q . K^_j = n_j (H (s_K * q)) . c_K[code_j] / sqrt(d): q is rotated once per
+// head (q' = H (s_K * q)) and every score is a dot product of q' with codebook entries.  With
+// V^_j = s_V * H (n_j c_V[code_j]) / sqrt(d), sum_j p_j V^_j = s_V * H (sum_j p_j n_j c_V[code_j]) /
+// sqrt(d): P.V is accumulated in the rotated domain and rotated back once per head, after the
+// splits are merged.
+//
+// Both products run on the int8 MFMA (v_mfma_i32_16x16x64_i8) in the digit form of the int8
+// decode:
+//   * codebook entries as three signed 7-bit digits of c 2^-E, looked up per byte with v_perm_b32
+//     from 16-byte digit tables (4 entries for 2-bit codes: one permute; 16 entries for 4-bit
+//     codes: two permutes and a byte select);
+//   * q' as four signed 7-bit digits under a per-head power of two (B of S = K q'), and
+//     P~_j = p_j n^V_j as four unsigned 7-bit digits of P~ / 2^F rounded at 28 bits (B of
+//     O' += V^T P~), one MFMA column per (digit, head) for 4 heads;
+//   * one accumulator per codebook digit; the digit columns are recombined in fp32.
+// Sums of digit products are exact integers; what is rounded is the codebook (to 21 fractional
+// bits of 2^E), q' and P~ (to 28 bits of their scale) and the fp32 recombination.
+//
+// Pass 1 (tq_attn_partial_kernel), grid (splits, bh_kv, ceil(G/4)): 4 waves stream 64-key tiles
+// of one KV head (K codes straight into the MFMA operand layout, V codes through a wave-private
+// LDS slot for the transposing byte reads) and leave (m, l, O') per (query head, split).
+// Pass 2 (tq_attn_merge_kernel): per query head, the log-sum-exp merge of the splits, 1/l, the
+// inverse rotation O = s_V * H O' / sqrt(d), the epilogue and the store.
+#include "device_common.hpp"
+
+namespace fa {
+namespace {
+
+constexpr float kTqLazyLog2 = 8.0f;
+constexpr int kTqWaves = 4;
+constexpr int kTqFlushTiles = 1024;   // P~V accumulators: 1024 tiles x 64 keys x 127 x 64 < 2^31
+
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+typedef int i32x2t __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) i32x2t lds_i32x2t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8t;
+
+// Byte lookups of four code bytes (one code per byte, values below 2^BITS) in a digit table.
+template <int BITS>
+__device__ __forceinline__ unsigned lookup4(unsigned sel, const uint32_t (&tab)[4]) {
+  if constexpr (BITS == 2) {
+    return __builtin_amdgcn_perm(tab[0], tab[0], sel);                 // selectors 0..3: entries 0..3
+  } else {
+    const unsigned s7 = sel & 0x07070707u;
+    const unsigned lo = __builtin_amdgcn_perm(tab[1], tab[0], s7);     // entries 0..7
+    const unsigned hi = __builtin_amdgcn_perm(tab[3], tab[2], s7);     // entries 8..15
+    const unsigned pick = ((sel >> 1) & 0x04040404u) | 0x03020100u;    // byte i: i (lo) or 4 + i (hi)
+    return __builtin_amdgcn_perm(hi, lo, pick);
+  }
+}
+
+template <int D, int KBITS, int VBITS>
+struct TqCfg {
+  static constexpr int KT = 64;                       // keys per tile
+  static constexpr int KG = 16;                       // keys per lane group
+  static constexpr int NKB = KT / 16;                 // 16-key row blocks of S
+  static constexpr int NKK = D / 64;                  // 64-deep k-steps of S
+  static constexpr int RK = D * KBITS / 8;            // K code bytes per key
+  static constexpr int QBK = RK / 4;                  // K code bytes per lane group and key
+  static constexpr int KW = QBK / 4;                  // ... as 32-bit words
+  static constexpr int RV = D * VBITS / 8;            // V code bytes per key
+  static constexpr int NC16V = RV / 16;               // 16-byte chunks per V row
+  static constexpr int VCH = KT * NC16V / 64;         // 16-byte V loads per lane per tile
+  static constexpr int FV = 8 / VBITS;                // codes per V byte
+  static constexpr int NBLK = NC16V * FV;             // 16-channel blocks of O' (= D / 16)
+  static constexpr int SP = NC16V >= 8 ? 8 : NC16V >= 4 ? 4 : NC16V >= 2 ? 2 : 1;   // LDS swizzle span
+  static constexpr int SLOT = KT * RV + 8 * KT;       // wave-private LDS bytes (V tile, norms)
+  static_assert(NBLK == D / 16, "block count");
+  static_assert(QBK % 4 == 0 && NC16V >= 1, "layout");
+};
+
+template <int SP>
+__device__ __forceinline__ int tswz(int r) {
+  return ((r >> 1) ^ (r >> 4)) & (SP - 1);
+}
+
+// Channel of k-slot s (0..15) of lane group hq in k-step kk: the lane's A bytes come from its
+// code words in the order the lookups produce them (4-bit: low nibbles then high nibbles of each
+// word; 2-bit: field 0 of the four bytes, then field 1, ...).
+template <int D, int KBITS>
+__device__ __forceinline__ int k_slot_channel(int kk, int hq, int s) {
+  const int base = hq * (D / 4) + 16 * kk;
+  const int w = s >> 2, e = s & 3;
+  if constexpr (KBITS == 4) return base + 8 * (w >> 1) + 2 * e + (w & 1);
+  else return base + 4 * e + w;
+}
+
+template <int D, int KBITS, int VBITS>
+__global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAttnArgs a) {
+  using C = TqCfg<D, KBITS, VBITS>;
+  constexpr int KT = C::KT, KG = C::KG, NKB = C::NKB, NKK = C::NKK, RK = C::RK, QBK = C::QBK, KW = C::KW;
+  constexpr int RV = C::RV, NC16V = C::NC16V, VCH = C::VCH, FV = C::FV, NBLK = C::NBLK, SP = C::SP;
+  constexpr int HPW = 4;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds_slot[kTqWaves][C::SLOT];
+  __shared__ float lds_q[HPW][D];        // s_K * q, then q' = H (s_K * q)
+  __shared__ float lds_m[kTqWaves][HPW];
+  __shared__ float lds_l[kTqWaves][HPW];
+  __shared__ float lds_o[kTqWaves][HPW][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int hq = lane >> 4;
+  const int t_dig = n >> 2;
+  const int gq = n & 3;
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int zh = blockIdx.z * HPW;
+  const int nh = min(HPW, a.group - zh);
+  const int64_t kv_base = (int64_t)kvh * a.s_k;
+  const int head0 = kvh * a.group + zh;
+
+  // ---- q' = H (s_K * q) for the workgroup's heads (absent heads are zero)
+  for (int i = tid; i < HPW * D; i += 64 * kTqWaves) {
+    const int g = i / D, j = i % D;
+    float x = 0.f;
+    if (g < nh) {
+      const int64_t at = (int64_t)(head0 + g) * D + j;
+      x = a.q_bf16 ? bf16_bits_to_f32(static_cast<const unsigned short*>(a.q)[at]) : static_cast<const float*>(a.q)[at];
+      x = a.ks[j] < 0 ? -x : x;
+    }
+    lds_q[g][j] = x;
+  }
+  __syncthreads();
+  constexpr int QR = HPW * D / (64 * kTqWaves);   // q' entries per thread
+  float qp[QR];
+#pragma unroll
+  for (int r = 0; r < QR; ++r) {
+    const int i = tid + 64 * kTqWaves * r;
+    const int g = i / D, row = i % D;
+    float acc = 0.f;
+    for (int j = 0; j < D; ++j) {
+      const float v = lds_q[g][j];
+      acc += (__popc(row & j) & 1) ? -v : v;
+    }
+    qp[r] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < QR; ++r) {
+    const int i = tid + 64 * kTqWaves * r;
+    lds_q[i / D][i % D] = qp[r];
+  }
+  __syncthreads();
+
+  // ---- q' digit B operands (column n = (t_dig, gq), k-slots in the K lookup order)
+  i32x4 qdig[NKK];
+  float s_comb;   // 2^(E_q + E_k - 7 (t + 1) - 7) / sqrt(d) for this lane's digit column
+  {
+    float qv[NKK][16];
+    float mx = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        qv[kk][s] = lds_q[gq][k_slot_channel<D, KBITS>(kk, hq, s)];
+        mx = fmaxf(mx, fabsf(qv[kk][s]));
+      }
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    int E = 0;
+    if (mx > 0.f) {
+      (void)frexpf(mx, &E);
+      E += 1;
+    }
+    s_comb = ldexpf(1.0f / sqrtf((float)D), E + a.k_e - 7 * (t_dig + 1) - 7);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      unsigned w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        float x = ldexpf(qv[kk][s], -E) * 128.f;
+        float dd[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          dd[t] = __builtin_rintf(x);
+          x = (x - dd[t]) * 128.f;
+        }
+        const int dig = (int)(t_dig == 0 ? dd[0] : t_dig == 1 ? dd[1] : t_dig == 2 ? dd[2] : dd[3]);
+        w[s / 4] |= ((unsigned)dig & 0xffu) << (8 * (s % 4));
+      }
+      qdig[kk] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  }
+
+  uint32_t ktab[3][4], vtab[3][4];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ktab[t][e] = a.ktab[t][e];
+      vtab[t][e] = a.vtab[t][e];
+    }
+
+  // ---- tiles of this split; wave w takes tiles w, w + 4, ...
+  const int n_tiles_total = (a.s_k - a.key_lo + KT - 1) / KT;
+  const int ts = split * a.tiles_per_split;
+  const int te = min(n_tiles_total, ts + a.tiles_per_split);
+  const int n_w = te > ts + wave ? (te - ts - wave + kTqWaves - 1) / kTqWaves : 0;
+  const int last_key = a.s_k - 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // K: row block kb, lane n is key KG (n/4) + 4 kb + n%4 (so the score accumulator's lane group
+  // hq owns keys KG hq .. KG hq + KG - 1, the keys the transposing V reads give it); the lane
+  // loads its group's QBK bytes of that row.  V: 16-byte chunk F = 64 u + lane of the tile's
+  // contiguous rows.  Norms: entry 64 e + lane of [K norms | V norms].
+  struct Tile {
+    uint32_t k[NKB][KW];
+    u32x4 v[VCH];
+    float nrm[2];
+  };
+  int krow[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) krow[kb] = KG * (n >> 2) + 4 * kb + (n & 3);
+  auto load = [&](int idx, Tile& T) {
+    const int k0 = a.key_lo + (ts + wave_u + kTqWaves * idx) * KT;
+    const int lim = last_key - k0;
+    const uint8_t* kt = a.kc + (kv_base + k0) * RK + hq * QBK;
+    const uint8_t* vt = a.vc + (kv_base + k0) * RV;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint8_t* p = kt + min(krow[kb], lim) * RK;
+      if constexpr (KW % 4 == 0) {
+#pragma unroll
+        for (int w4 = 0; w4 < KW / 4; ++w4) {
+          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + w4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) T.k[kb][4 * w4 + e] = x[e];
+        }
+      } else if constexpr (KW == 2) {
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        T.k[kb][0] = x[0];
+        T.k[kb][1] = x[1];
+      } else {
+        T.k[kb][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int F = 64 * u + lane;
+      const int o = min(F / NC16V, lim) * RV + 16 * (F % NC16V);
+      T.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + o));
+    }
+    const int r = min(lane, lim);
+    T.nrm[0] = __builtin_nontemporal_load(a.kn + kv_base + k0 + r);
+    T.nrm[1] = __builtin_nontemporal_load(a.vn + kv_base + k0 + r);
+  };
+  unsigned char* slot = &lds_slot[wave][0];
+
+  // O' = Of + sum_t Oi[t] 2^(F + E_v - 7 (t_q + 1) - 7 (t + 1)): Oi exact int32 sums since the last
+  // flush (one per codebook digit t), Of the fp32 total before it.
+  float Of[NBLK][4];
+  i32x4 Oi[NBLK][3];
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) Oi[b][t] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Of[b][v] = 0.f;
+  }
+  float m_run = neg_inf(), l_run = 0.f, mc = 0.f;
+  int F = -1000;
+  int since_flush = 0;
+  const float c2 = a.scale_log2;
+  const float lazy_thr = kTqLazyLog2 / c2;
+  auto flush = [&]() {
+    const int ex = F + a.v_e - 7 * (t_dig + 1) - 7;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float y = __builtin_fmaf((float)Oi[b][2][v], 1.0f / 128.f, (float)Oi[b][1][v]);
+        y = __builtin_fmaf(y, 1.0f / 128.f, (float)Oi[b][0][v]);
+        Of[b][v] += ldexpf(y, ex);
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t) Oi[b][t] = i32x4{0, 0, 0, 0};
+    }
+    since_flush = 0;
+  };
+
+  auto compute = [&](int idx, bool valid, const Tile& T) {
+    const int k0 = a.key_lo + (ts + wave_u + kTqWaves * idx) * KT;
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int Fc = 64 * u + lane;
+      const int r = Fc / NC16V;
+      *reinterpret_cast<u32x4*>(slot + r * RV + 16 * ((Fc % NC16V) ^ tswz<SP>(r))) = T.v[u];
+    }
+    reinterpret_cast<float*>(slot + KT * RV)[lane] = T.nrm[0];
+    reinterpret_cast<float*>(slot + KT * RV)[64 + lane] = T.nrm[1];
+    const float* snk = reinterpret_cast<const float*>(slot + KT * RV);
+    const float* snv = snk + KT;
+    float kn[NKB][4], vn[NKB][4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(snk + KG * hq + 4 * kb);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(snv + KG * hq + 4 * kb);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        kn[kb][v] = x[v];
+        vn[kb][v] = y[v];
+      }
+    }
+    const bool tail = !valid || k0 + KT > a.s_k;
+    const int key_lim = valid ? last_key - k0 - KG * hq : -1;
+
+    // S: per row block, one accumulator per codebook digit, the k-steps accumulated in it
+    float s[NKB][4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      i32x4 acc[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        unsigned sel[4];
+        if constexpr (KBITS == 4) {
+          const unsigned w0 = T.k[kb][2 * kk], w1 = T.k[kb][2 * kk + 1];
+          sel[0] = w0 & 0x0f0f0f0fu;
+          sel[1] = (w0 >> 4) & 0x0f0f0f0fu;
+          sel[2] = w1 & 0x0f0f0f0fu;
+          sel[3] = (w1 >> 4) & 0x0f0f0f0fu;
+        } else {
+          const unsigned w = T.k[kb][kk];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sel[c] = (w >> (2 * c)) & 0x03030303u;
+        }
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const i32x4 av = {(int)lookup4<KBITS>(sel[0], ktab[t]), (int)lookup4<KBITS>(sel[1], ktab[t]),
+                            (int)lookup4<KBITS>(sel[2], ktab[t]), (int)lookup4<KBITS>(sel[3], ktab[t])};
+          acc[t] = mfma16_i8(av, qdig[kk], acc[t]);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float y = __builtin_fmaf((float)acc[2][v], 1.0f / 128.f, (float)acc[1][v]);
+        y = __builtin_fmaf(y, 1.0f / 128.f, (float)acc[0][v]);
+        y *= s_comb;
+        y = y + row_ror<8>(y);
+        y = y + row_ror<4>(y);
+        s[kb][v] = y * kn[kb][v];
+      }
+    }
+    if (tail) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (4 * kb + v > key_lim) s[kb][v] = neg_inf();
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    const bool raised = __any(mx - m_run > lazy_thr);
+    if (raised) {
+      flush();
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Of[b][v] *= alpha;
+      m_run = m_new;
+      mc = m_use * c2;
+    }
+    float pt[NKB][4];
+    float ps = 0.f, pmax = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], c2, -mc));
+        ps += p;
+        pt[kb][v] = p * vn[kb][v];
+        pmax = fmaxf(pmax, pt[kb][v]);
+      }
+    l_run += ps;
+    pmax = max_xor16(pmax);
+    pmax = max_xor32(pmax);
+    int Fp = -1000;
+    if (pmax > 0.f) (void)frexpf(pmax, &Fp);
+    const bool grow = __any(Fp > F) || since_flush >= kTqFlushTiles;
+    if (grow && !raised) flush();
+    if (raised || grow) F = Fp + 1;
+    ++since_flush;
+    // digit t_q of x = P~ / 2^F in [0, 1): bits 21 - 7 t_q .. 27 - 7 t_q of rint(x 2^28); k-slot
+    // 4 kb + v of lane group hq is key KG hq + 4 kb + v
+    const int sh = 21 - 7 * t_dig;
+    unsigned pw[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      unsigned w = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const unsigned qx = (unsigned)__builtin_rintf(ldexpf(pt[kb][v], 28 - F));
+        w |= ((qx >> sh) & 0x7fu) << (8 * v);
+      }
+      pw[kb] = w;
+    }
+    const i32x4 pdig = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+
+    // O'^T: byte column 16 b + n of the V rows holds codes FV (16 b + n) + c; the transposing
+    // reads give lane n those bytes for keys KG hq .. KG hq + 15.
+#pragma unroll
+    for (int b = 0; b < NC16V; ++b) {
+      int w4[4];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int vrow = KG * hq + 8 * h8 + (n >> 1);
+        const int off = vrow * RV + 16 * (b ^ tswz<SP>(vrow)) + 8 * (n & 1);
+        const i32x2t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2t*)((lds_u8t*)slot + off));
+        w4[2 * h8] = r[0];
+        w4[2 * h8 + 1] = r[1];
+      }
+#pragma unroll
+      for (int c = 0; c < FV; ++c) {
+        unsigned sel[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sel[e] = ((unsigned)w4[e] >> (VBITS * c)) & (VBITS == 4 ? 0x0f0f0f0fu : 0x03030303u);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const i32x4 av = {(int)lookup4<VBITS>(sel[0], vtab[t]), (int)lookup4<VBITS>(sel[1], vtab[t]),
+                            (int)lookup4<VBITS>(sel[2], vtab[t]), (int)lookup4<VBITS>(sel[3], vtab[t])};
+          Oi[b * FV + c][t] = mfma16_i8(av, pdig, Oi[b * FV + c][t]);
+        }
+      }
+    }
+  };
+
+  constexpr int NT = 2;
+  Tile T[NT];
+  if (n_w > 0) {
+    load(0, T[0]);
+    for (int base = 0; base < n_w; base += NT) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int idx = base + j;
+        load(min(idx + 1, n_w - 1), T[(j + 1) % NT]);
+        compute(idx, idx < n_w, T[j]);
+      }
+    }
+  }
+
+  // ---- combine digit columns and lane groups, then the waves through LDS.  Block b * FV + c,
+  // row 4 hq + v is channel FV (16 b + 4 hq + v) + c.
+  flush();
+  float lt = l_run;
+  lt = add_xor16(lt);
+  lt = add_xor32(lt);
+  if (lane == gq) {
+    lds_m[wave][gq] = m_run;
+    lds_l[wave][gq] = lt;
+  }
+#pragma unroll
+  for (int b = 0; b < NC16V; ++b)
+#pragma unroll
+    for (int c = 0; c < FV; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float y = Of[b * FV + c][v];
+        y = y + row_ror<8>(y);
+        y = y + row_ror<4>(y);
+        if (t_dig == 0) lds_o[wave][gq][FV * (16 * b + 4 * hq + v) + c] = y;
+      }
+  __syncthreads();
+
+  for (int idx = tid; idx < nh * (D + 2); idx += 64 * kTqWaves) {
+    const int hz = idx / (D + 2), col = idx % (D + 2);
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kTqWaves; ++w) M = fmaxf(M, lds_m[w][hz]);
+    float acc = 0.f;
+    if (col == 0) {
+      acc = M;
+    } else if (M != neg_inf()) {
+#pragma unroll
+      for (int w = 0; w < kTqWaves; ++w) {
+        const float wt = __builtin_amdgcn_exp2f((lds_m[w][hz] - M) * c2);
+        acc += wt * (col == 1 ? lds_l[w][hz] : lds_o[w][hz][col - 2]);
+      }
+    }
+    const int64_t head = head0 + hz;
+    a.partial[(head * a.num_splits + split) * (D + 2) + col] = acc;
+  }
+}
+
+// Pass 2: one workgroup of 64 lanes per query head.  The merged O' / L goes through LDS and each
+// lane forms its outputs x_i = s_V[i] sum_j H[i][j] O'_j / sqrt(d).
+template <int D>
+__global__ __launch_bounds__(64) void tq_attn_merge_kernel(TqAttnArgs a) {
+  constexpr int PER = D / 64;
+  __shared__ float o_rot[D];
+  const int lane = threadIdx.x;
+  const int head = blockIdx.x;
+  const float c2 = a.scale_log2;
+  const int S = a.num_splits;
+  const float* p = a.partial + (int64_t)head * S * (D + 2);
+  float M = neg_inf();
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+  float L = 0.f;
+  float o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+  if (M != neg_inf()) {
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) {
+      const float* ps = p + (int64_t)s * (D + 2);
+      const float w = __builtin_amdgcn_exp2f((ps[0] - M) * c2);
+      L += w * ps[1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] += w * ps[2 + lane + 64 * e];
+    }
+  }
+  const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o_rot[lane + 64 * e] = o[e] * inv;
+  __syncthreads();
+  const float rs = 1.0f / sqrtf((float)D);
+  float y[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int i = lane + 64 * e;
+    float acc = 0.f;
+    for (int j = 0; j < D; ++j) {
+      const float v = o_rot[j];
+      acc += (__popc(i & j) & 1) ? -v : v;
+    }
+    acc *= rs;
+    y[e] = a.vs[i] < 0 ? -acc : acc;
+  }
+  apply_epilogue_all(y, a.epi, [&](int e) { return lane + 64 * e; });
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane + 64 * e;
+    if (a.out_bf16) static_cast<__bf16*>(a.out)[(int64_t)head * D + d] = (__bf16)y[e];
+    else static_cast<float*>(a.out)[(int64_t)head * D + d] = y[e];
+  }
+  if (a.lse && lane == 0) a.lse[head] = L > 0.f ? M * a.scale + logf(L) : neg_inf();
+}
+
+template <int D, int KB, int VB>
+hipError_t launch_tq_attn_d(const TqAttnArgs& a_in, hipStream_t st, const char** name) {
+  TqAttnArgs a = a_in;
+  constexpr int KT = TqCfg<D, KB, VB>::KT;
+  const int tiles = (a.s_k - a.key_lo + KT - 1) / KT;
+  a.tiles_per_split = (tiles + a.num_splits - 1) / a.num_splits;
+  const dim3 grid((unsigned)a.num_splits, (unsigned)a.bh_kv, (unsigned)((a.group + 3) / 4));
+  hipLaunchKernelGGL((tq_attn_partial_kernel<D, KB, VB>), grid, dim3(64 * kTqWaves), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tq_attn_merge_kernel<D>), dim3((unsigned)a.bh_q), dim3(64), 0, st, a);
+  *name = "tq_attention_decode";
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_tq_attn_bits(const TqAttnArgs& a, int kb, int vb, hipStream_t st, const char** name) {
+  if (kb == 4 && vb == 2) return launch_tq_attn_d<D, 4, 2>(a, st, name);
+  if (kb == 4 && vb == 4) return launch_tq_attn_d<D, 4, 4>(a, st, name);
+  if (kb == 2 && vb == 2) return launch_tq_attn_d<D, 2, 2>(a, st, name);
+  if (kb == 2 && vb == 4) return launch_tq_attn_d<D, 2, 4>(a, st, name);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_tq_attention(const TqAttnArgs& a, int32_t d, int32_t kbits, int32_t vbits, hipStream_t st,
+                               const char** name) {
+  if (a.bh_kv > 65535 || (a.group + 3) / 4 > 65535) return hipErrorInvalidConfiguration;
+  switch (d) {
+    case 64: return launch_tq_attn_bits<64>(a, kbits, vbits, st, name);
+    case 128: return launch_tq_attn_bits<128>(a, kbits, vbits, st, name);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa
