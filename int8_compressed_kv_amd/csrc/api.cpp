@@ -469,8 +469,9 @@ int32_t fa_tq_attention_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int
   const int32_t group = bh_q / bh_kv;
   const int64_t units = (int64_t)bh_kv * ((group + 3) / 4);
   const int32_t tiles = (s_k + kTqAttnTile - 1) / kTqAttnTile;
-  // one workgroup per CU (256), each split keeping at least 8 tiles (2 per wave)
-  int64_t splits = (256 + units - 1) / units;
+  // about 1024 workgroups (two fit on a CU at once, and the surplus evens out the tail), each
+  // split keeping at least 8 tiles (2 per wave)
+  int64_t splits = (1024 + units - 1) / units;
   const int64_t max_by_len = tiles / 8 > 0 ? tiles / 8 : 1;
   if (splits > max_by_len) splits = max_by_len;
   if (splits > kMaxSplits) splits = kMaxSplits;

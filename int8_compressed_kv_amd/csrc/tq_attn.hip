@@ -97,7 +97,8 @@ __device__ __forceinline__ int k_slot_channel(int kk, int hq, int s) {
 }
 
 template <int D, int KBITS, int VBITS>
-__global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAttnArgs a) {
+__global__ __launch_bounds__(64 * kTqWaves, (D == 128 && KBITS == 4 && VBITS == 4) ? 1 : 2)   // 4/4 needs > 256 VGPRs
+void tq_attn_partial_kernel(TqAttnArgs a) {
   using C = TqCfg<D, KBITS, VBITS>;
   constexpr int KT = C::KT, KG = C::KG, NKB = C::NKB, NKK = C::NKK, RK = C::RK, QBK = C::QBK, KW = C::KW;
   constexpr int RV = C::RV, NC16V = C::NC16V, VCH = C::VCH, FV = C::FV, NBLK = C::NBLK, SP = C::SP;
@@ -305,17 +306,6 @@ __global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAtt
     reinterpret_cast<float*>(slot + KT * RV)[64 + lane] = T.nrm[1];
     const float* snk = reinterpret_cast<const float*>(slot + KT * RV);
     const float* snv = snk + KT;
-    float kn[NKB][4], vn[NKB][4];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(snk + KG * hq + 4 * kb);
-      const f32x4 y = *reinterpret_cast<const f32x4*>(snv + KG * hq + 4 * kb);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        kn[kb][v] = x[v];
-        vn[kb][v] = y[v];
-      }
-    }
     const bool tail = !valid || k0 + KT > a.s_k;
     const int key_lim = valid ? last_key - k0 - KG * hq : -1;
 
@@ -345,6 +335,7 @@ __global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAtt
           acc[t] = mfma16_i8(av, qdig[kk], acc[t]);
         }
       }
+      const f32x4 kn = *reinterpret_cast<const f32x4*>(snk + KG * hq + 4 * kb);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float y = __builtin_fmaf((float)acc[2][v], 1.0f / 128.f, (float)acc[1][v]);
@@ -352,7 +343,7 @@ __global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAtt
         y *= s_comb;
         y = y + row_ror<8>(y);
         y = y + row_ror<4>(y);
-        s[kb][v] = y * kn[kb][v];
+        s[kb][v] = y * kn[v];
       }
     }
     if (tail) {
@@ -386,14 +377,16 @@ __global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAtt
     float pt[NKB][4];
     float ps = 0.f, pmax = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      const f32x4 vn = *reinterpret_cast<const f32x4*>(snv + KG * hq + 4 * kb);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], c2, -mc));
         ps += p;
-        pt[kb][v] = p * vn[kb][v];
+        pt[kb][v] = p * vn[v];
         pmax = fmaxf(pmax, pt[kb][v]);
       }
+    }
     l_run += ps;
     pmax = max_xor16(pmax);
     pmax = max_xor32(pmax);
@@ -447,17 +440,15 @@ __global__ __launch_bounds__(64 * kTqWaves, 1) void tq_attn_partial_kernel(TqAtt
     }
   };
 
-  constexpr int NT = 2;
-  Tile T[NT];
+  // one tile in flight while the current one is computed; the loads past the end repeat the
+  // last tile
   if (n_w > 0) {
-    load(0, T[0]);
-    for (int base = 0; base < n_w; base += NT) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int idx = base + j;
-        load(min(idx + 1, n_w - 1), T[(j + 1) % NT]);
-        compute(idx, idx < n_w, T[j]);
-      }
+    Tile cur, nxt;
+    load(0, cur);
+    for (int idx = 0; idx < n_w; ++idx) {
+      load(min(idx + 1, n_w - 1), nxt);
+      compute(idx, true, cur);
+      cur = nxt;
     }
   }
 
