@@ -386,10 +386,21 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     return f16x2{hv, hv};
   };
 
+  // Staging order of the 16-code chunks of a tile (head_dim 64 / 128): position pos holds chunk
+  // pos % NCR of row staged_row(pos).  Each block of 8 rows is staged in the row order
+  // 0, 4, 1, 5, 2, 6, 3, 7, so the 16 threads of a quarter-wave, which convert 16 consecutive
+  // positions, cover rows whose swizzles differ in bit 0 (row bit 2): their 16-byte operand writes
+  // then fall into distinct bank groups, while their reads of the staging stage stay contiguous.
+  constexpr int NCR = D / 16;   // 16-code chunks per row
+  auto staged_row = [&](int pos) __attribute__((always_inline)) {
+    const int blk = pos / (8 * NCR), slot = (pos % (8 * NCR)) / NCR;
+    return 8 * blk + (slot >> 1) + 4 * (slot & 1);
+  };
+
   if constexpr (DMA) {
     // Per tile: wave w copies K/V segments SPW w .. SPW w + SPW - 1 (segment gs < SEGS is K
-    // segment gs, else V segment gs - SEGS; lane l of a segment brings the 16 codes at byte
-    // 1024 seg + 16 l of the row-major tile), wave 0 the 64 k scales and wave 1 the 64 v scales.
+    // segment gs, else V segment gs - SEGS; lane l of a segment brings the 16 codes of staging
+    // position 64 seg + l), wave 0 the 64 k scales and wave 1 the 64 v scales.
     // Tile t + 3's copies are issued in iteration t, after the barrier that ended the conversion
     // of tile t - 1 (the last reader of that staging stage, in iteration t - 2); each wave waits
     // for its own copies of tile t + 3 at the end of iteration t + 1, before the barrier that
@@ -403,10 +414,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     for (int j = 0; j < SPW; ++j) {
       const int gs = SPW * wave + j;
       const int mat = gs / SEGS, seg = gs % SEGS;
-      const int p = 1024 * seg + 16 * lane;
-      crow[j] = p / D;
-      ccol[j] = p % D;
-      voff[j] = (unsigned)p;
+      const int pos = 64 * seg + lane;            // 16-byte staging position within the matrix
+      crow[j] = staged_row(pos);
+      ccol[j] = 16 * (pos % NCR);
+      voff[j] = (unsigned)(crow[j] * D + ccol[j]);
       cbase[j] = mat ? vp8 : kp8;
       seg_lds[j] = __builtin_amdgcn_readfirstlane(q8_0 + (unsigned)(mat * BN * D + 1024 * seg));
     }
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
         const bool is_v = ci >= NCH8 / 2;
         const int cm = is_v ? ci - NCH8 / 2 : ci;
         const u32x4 w = *reinterpret_cast<const u32x4*>(&lds_q8[static_cast<int>(s8)][16 * ci]);
-        const int r = (16 * cm) / D, lc = 2 * ((16 * cm) % D / 16);
+        const int r = staged_row(cm), lc = 2 * (cm % NCR);
         const f16x2 sr = half2_of(lds_s8[static_cast<int>(s8)][(is_v ? BN : 0) + r] * (is_v ? vs_norm : ks_norm));
         const u32x2 x0 = scaled4(w[0], sr), x1 = scaled4(w[1], sr);
         const u32x2 x2 = scaled4(w[2], sr), x3 = scaled4(w[3], sr);
