@@ -194,3 +194,14 @@ def _abs_variant(orig, x, ops):
     for k, v in ops:
         y = np.abs(y) if k == "relu" else orig(y, [(k, v)])
     return y
+
+
+def test_rope_with_the_sine_sign_flipped_is_caught_by_the_hand_fixture():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rope_rotate_half_hand.json")))
+    x = np.array(g["x"], np.float32)
+    wrong = oracle.rope_rotate_half(x, g["cos"], [-v for v in g["sin"]])   # rotation the other way
+    assert wrong.tolist() != g["out"]
+    swapped = oracle.rope_rotate_half(x[[2, 3, 0, 1]], g["cos"], g["sin"])[[2, 3, 0, 1]]   # halves swapped
+    assert swapped.tolist() != g["out"]

@@ -478,3 +478,57 @@ def test_bias_relu_chain_matches_brute_force():
     o, _ = oracle.attention(q, k, v, causal=True, epilogue=ops)
     assert np.abs(o - o_ref).max() < 1e-13
     assert (o_ref == -0.25).any() and (o_ref > -0.25).any()     # the relu both clipped and passed
+
+
+# ---- rotate-half RoPE in the cache write (FlashRT QKV Cache RoPE: the decode K write)
+
+def _angles(n_pos, d, base=10000.0):
+    inv = base ** (-np.arange(0, d // 2, dtype=np.float64) * 2.0 / d)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def test_rope_hand_worked_fixture():
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rope_rotate_half_hand.json")))
+    out = oracle.rope_rotate_half(np.array(g["x"], np.float32), g["cos"], g["sin"])
+    assert out.tolist() == g["out"]
+
+
+def test_rope_identity_norms_and_relative_positions():
+    rng = np.random.Generator(np.random.PCG64(41))
+    d = 64
+    cos, sin = _angles(300, d)
+    x = rng.standard_normal((5, d)).astype(np.float32)
+    # position 0: cos 1, sin 0 leaves every value unchanged, bit for bit
+    assert np.array_equal(oracle.rope_rotate_half(x, cos[0], sin[0]), x)
+    # a rotation in each (i, i + d/2) plane keeps the norm (up to fp32 rounding)
+    y = oracle.rope_rotate_half(x, cos[123], sin[123])
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-6)
+    # <R_m q, R_n k> depends on m - n only
+    q, k = x[0], x[1]
+    a = float(np.dot(oracle.rope_rotate_half(q, cos[200], sin[200]), oracle.rope_rotate_half(k, cos[150], sin[150])))
+    b = float(np.dot(oracle.rope_rotate_half(q, cos[50], sin[50]), oracle.rope_rotate_half(k, cos[0], sin[0])))
+    assert abs(a - b) < 1e-4 * (np.linalg.norm(q) * np.linalg.norm(k))
+
+
+def test_append_with_rope_rotates_k_only_and_equals_quantizing_the_rotated_rows():
+    rng = np.random.Generator(np.random.PCG64(42))
+    bh, cap, d, n_new = 2, 10, 32, 3
+    cos, sin = _angles(cap, d)
+    k_new = rng.standard_normal((bh, n_new, d)).astype(np.float32)
+    v_new = rng.standard_normal((bh, n_new, d)).astype(np.float32)
+    z8, z = np.zeros((bh, cap, d), np.int8), np.zeros((bh, cap), np.float32)
+    pos = np.array([4, 8])
+    kc, vc, ks, vs = oracle.append_kv(z8, z8, z, z, k_new, v_new, pos, rope_cos=cos, rope_sin=sin)
+    kc0, vc0, ks0, vs0 = oracle.append_kv(z8, z8, z, z, k_new, v_new, pos)
+    assert np.array_equal(vc, vc0) and np.array_equal(vs, vs0)
+    for b in range(bh):
+        for j in range(n_new):
+            p = pos[b] + j
+            if p >= cap:
+                continue                      # past the end: skipped (row 9 holds token 1 of head 1)
+            q, s = oracle.quantize_per_token(oracle.rope_rotate_half(k_new[b, j], cos[p], sin[p]))
+            assert np.array_equal(kc[b, p], q) and ks[b, p] == s
+            assert not np.array_equal(kc[b, p], kc0[b, p])   # the rotation changed the codes
+    assert not kc[1, :8].any() and not kc[0, 7:].any()
