@@ -119,6 +119,23 @@ int fa_append_kv(const void* k_new, const void* v_new, int32_t x_dtype, int32_t 
                  float* k_scale, float* v_scale, void* stream);
 
 /*
+ * fa_append_kv_rope -- fa_append_kv with the new K rows first rotated by rotate-half RoPE at their
+ * cache position (FlashRT QKV Cache RoPE, Kernels list: the decode K write applies rotate-half RoPE
+ * with half-width cos/sin vectors and selects the slot from a device position).
+ *   rope_cos, rope_sin  device fp32 [capacity, head_dim / 2], 16-byte aligned: row p holds the
+ *                       cos / sin of cache position p.  Both NULL: no rotation (fa_append_kv).
+ * For channel i < head_dim / 2 and the K row x written at position p:
+ *   x'_i = x_i cos[p][i] - x_{i+d/2} sin[p][i],  x'_{i+d/2} = x_{i+d/2} cos[p][i] + x_i sin[p][i],
+ * each product and the sum a separately rounded fp32 operation; x' is then quantized exactly as
+ * fa_compress_kv quantizes a row.  V rows are written unrotated.  Other arguments, skipping and
+ * errors as for fa_append_kv.
+ */
+int fa_append_kv_rope(const void* k_new, const void* v_new, int32_t x_dtype, int32_t bh_kv, int32_t n_new,
+                      int32_t head_dim, const int32_t* pos, int32_t capacity, const float* rope_cos,
+                      const float* rope_sin, int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                      void* stream);
+
+/*
  * fa_forward -- attention forward for bh_q query heads over bh_kv KV heads.
  *   q        device, [bh_q, s_q, head_dim], q_dtype FA_F32 or FA_BF16.
  *   k, v     device, [bh_kv, s_k, head_dim], kv_dtype FA_F32, FA_BF16 or FA_I8.

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.fa_compress_kv.restype = ctypes.c_int
     L.fa_append_kv.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp]
     L.fa_append_kv.restype = ctypes.c_int
+    L.fa_append_kv_rope.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.fa_append_kv_rope.restype = ctypes.c_int
     L.fa_forward.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                              i32, i32, i32, i32, i32, f32, i32, i32, ctypes.POINTER(_EpiOp), i32, vp]
     L.fa_forward.restype = ctypes.c_int
@@ -240,10 +242,12 @@ def compress_kv(x, out=None, scales=None):
     return out, scales
 
 
-def append_kv(k_new, v_new, pos, k_cache, v_cache, k_scale, v_scale):
+def append_kv(k_new, v_new, pos, k_cache, v_cache, k_scale, v_scale, rope_cos=None, rope_sin=None):
     """Quantize new tokens k_new, v_new (bh_kv, n_new, d) fp32/bf16 into the int8 cache
     (bh_kv, capacity, d) with scales (bh_kv, capacity): token j of head b goes to row pos[b] + j,
-    pos an int32 device tensor (bh_kv,).  Rows outside the cache are skipped."""
+    pos an int32 device tensor (bh_kv,).  Rows outside the cache are skipped.  With rope_cos,
+    rope_sin (capacity, d/2) fp32 device tables, K rows are rotated (rotate-half RoPE at their
+    cache position) before they are quantized."""
     torch = _torch()
     if k_new.dim() != 3 or tuple(v_new.shape) != tuple(k_new.shape) or k_new.dtype != v_new.dtype:
         raise ValueError("k_new and v_new must be (bh_kv, n_new, head_dim) tensors of one dtype")
@@ -259,10 +263,19 @@ def append_kv(k_new, v_new, pos, k_cache, v_cache, k_scale, v_scale):
         raise ValueError("scales must be fp32")
     if pos.dtype != torch.int32 or tuple(pos.shape) != (bh_kv,):
         raise ValueError("pos must be an int32 tensor of shape (bh_kv,)")
-    _same_device(k_new, v_new=v_new, pos=pos, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale)
-    _check(lib().fa_append_kv(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new), bh_kv, n_new, d,
-                              _dev(pos, "pos"), cap, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                              _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream()))
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("give both rope_cos and rope_sin, or neither")
+    if rope_cos is not None:
+        if d % 2:
+            raise ValueError("RoPE needs an even head_dim")
+        _want(rope_cos, "rope_cos", (cap, d // 2), torch.float32)
+        _want(rope_sin, "rope_sin", (cap, d // 2), torch.float32)
+    _same_device(k_new, v_new=v_new, pos=pos, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale,
+                 rope_cos=rope_cos, rope_sin=rope_sin)
+    _check(lib().fa_append_kv_rope(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new), bh_kv, n_new, d,
+                                   _dev(pos, "pos"), cap, _dev(rope_cos, "rope_cos"), _dev(rope_sin, "rope_sin"),
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale"),
+                                   _dev(v_scale, "v_scale"), _stream()))
     return k_cache, v_cache, k_scale, v_scale
 
 

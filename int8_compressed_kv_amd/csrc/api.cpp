@@ -130,7 +130,19 @@ int fa_compress_kv(const void* x, int32_t x_dtype, int64_t n_tokens, int32_t hea
 int fa_append_kv(const void* k_new, const void* v_new, int32_t x_dtype, int32_t bh_kv, int32_t n_new,
                  int32_t head_dim, const int32_t* pos, int32_t capacity, int8_t* k_cache, int8_t* v_cache,
                  float* k_scale, float* v_scale, void* stream) {
+  return fa_append_kv_rope(k_new, v_new, x_dtype, bh_kv, n_new, head_dim, pos, capacity, nullptr, nullptr, k_cache,
+                           v_cache, k_scale, v_scale, stream);
+}
+
+int fa_append_kv_rope(const void* k_new, const void* v_new, int32_t x_dtype, int32_t bh_kv, int32_t n_new,
+                      int32_t head_dim, const int32_t* pos, int32_t capacity, const float* rope_cos,
+                      const float* rope_sin, int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                      void* stream) {
   g_last_error.clear();
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(FA_ERR_INVALID, "give both rope_cos and rope_sin, or neither");
+  if (rope_cos && ((reinterpret_cast<uintptr_t>(rope_cos) & 15u) || (reinterpret_cast<uintptr_t>(rope_sin) & 15u)))
+    return fail(FA_ERR_INVALID, "rope_cos and rope_sin must be 16-byte aligned");
   if (int r = check_head_dim(head_dim)) return r;
   if (x_dtype != FA_F32 && x_dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "append_kv input must be FA_F32 or FA_BF16 (got %d)", x_dtype);
@@ -152,6 +164,8 @@ int fa_append_kv(const void* k_new, const void* v_new, int32_t x_dtype, int32_t 
   a.v_cache = v_cache;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   a.bh_kv = bh_kv;
   a.n_new = n_new;
   a.capacity = capacity;

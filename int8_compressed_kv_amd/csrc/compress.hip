@@ -154,7 +154,12 @@ __global__ __launch_bounds__(256) void compress_kernel(const void* __restrict__ 
 // at advancing positions; one position per head also covers sequences of different lengths).
 // Global row r covers matrix r / (bh_kv n_new) (K, then V), head b and new token j; rows whose
 // cache position falls outside [0, capacity) are not written.
-template <int D, bool BF16_IN>
+// With ROPE, each K row is first rotated by rotate-half RoPE at its cache position p (FlashRT
+// QKV Cache RoPE: the decode K write rotates K before writing the slot): channel i < d/2 pairs
+// with i + d/2, out_i = x_i cos_i - x_{i+d/2} sin_i, out_{i+d/2} = x_{i+d/2} cos_i + x_i sin_i
+// (cos, sin = row p of the tables), each product and the sum rounded on its own.  The partner half
+// of a lane's chunk sits R/2 lanes away in the row's segment and is fetched by a lane shuffle.
+template <int D, bool BF16_IN, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int ELEM = BF16_IN ? 8 : 4;
   constexpr int R = D / ELEM;
@@ -174,9 +179,36 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int chunk = lane_on ? seg_lane : R - 1;
   float x[ELEM];
   load_chunk<BF16_IN, ELEM>(static_cast<const char*>(is_v ? a.v_new : a.k_new) + (rem * D + chunk * ELEM) * (BF16_IN ? 2 : 4), x);
+  const int p = a.pos[b] + j;
+  if constexpr (ROPE) {
+    constexpr int HALF = R / 2;                     // chunks per half row (D/2 is a multiple of ELEM)
+    const bool lower = chunk < HALF;
+    const int partner = (lane - seg_lane) + (lower ? chunk + HALF : chunk - HALF);
+    float xp[ELEM];
+#pragma unroll
+    for (int e = 0; e < ELEM; ++e) xp[e] = __shfl(x[e], partner, 64);   // every lane takes part
+    const int64_t prow = (int64_t)min(max(p, 0), a.capacity - 1) * (D / 2) + (lower ? chunk : chunk - HALF) * ELEM;
+    float cs[ELEM], sn[ELEM];
+#pragma unroll
+    for (int e4 = 0; e4 < ELEM / 4; ++e4) {
+      const f32x4 c4 = *reinterpret_cast<const f32x4*>(a.rope_cos + prow + 4 * e4);
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(a.rope_sin + prow + 4 * e4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cs[4 * e4 + e] = c4[e];
+        sn[4 * e4 + e] = s4[e];
+      }
+    }
+    if (!is_v) {
+#pragma unroll
+      for (int e = 0; e < ELEM; ++e) {
+        const float t = mul_rn(xp[e], sn[e]);
+        x[e] = add_rn(mul_rn(x[e], cs[e]), lower ? -t : t);
+      }
+    }
+  }
   unsigned packed[ELEM / 4];
   const float s = quantize_row<ELEM, SEG>(x, packed);
-  const int p = a.pos[b] + j;
   if (r < total && lane_on && p >= 0 && p < a.capacity) {
     const int64_t dst = (int64_t)b * a.capacity + p;
     store_codes<ELEM>((is_v ? a.v_cache : a.k_cache) + dst * D + seg_lane * ELEM, packed);
@@ -191,12 +223,15 @@ hipError_t launch_append_d(const AppendArgs& a, bool bf16, hipStream_t st, const
   const int64_t total = 2 * (int64_t)a.bh_kv * a.n_new;
   const int64_t blocks = (total + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const bool rope = a.rope_cos != nullptr;
   if (bf16) {
-    hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    *name = "append_bf16";
+    if (rope) hipLaunchKernelGGL((append_kernel<D, true, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((append_kernel<D, true, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    *name = rope ? "append_rope_bf16" : "append_bf16";
   } else {
-    hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    *name = "append_f32";
+    if (rope) hipLaunchKernelGGL((append_kernel<D, false, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((append_kernel<D, false, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    *name = rope ? "append_rope_f32" : "append_f32";
   }
   return hipGetLastError();
 }

@@ -66,6 +66,8 @@ struct AppendArgs {
   int8_t* v_cache;
   float* k_scale;       // [bh_kv, capacity]
   float* v_scale;
+  const float* rope_cos; // [capacity, d/2] rotate-half RoPE table of K by cache position, or null
+  const float* rope_sin;
   int32_t bh_kv, n_new, capacity;
 };
 

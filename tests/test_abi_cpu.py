@@ -278,3 +278,13 @@ def test_python_layer_checks_devices():
     q, k, v = torch.zeros(4, 8, 64), torch.zeros(2, 16, 64), torch.zeros(2, 16, 64, device="meta")
     with pytest.raises(ValueError, match="v is on meta"):
         fa.flash_attention(q, k, v)
+
+
+def test_append_rope_arguments_checked_on_host(L):
+    vp = ctypes.c_void_p
+    p = vp(1 << 20)
+    # only one of the two tables
+    assert L.fa_append_kv_rope(p, p, 0, 4, 1, 128, p, 100, p, None, p, p, p, p, None) == -1
+    # misaligned table
+    assert L.fa_append_kv_rope(p, p, 0, 4, 1, 128, p, 100, vp((1 << 20) + 4), p, p, p, p, p, None) == -1
+    assert L.fa_append_kv_rope(p, p, 0, 4, 0, 128, p, 100, p, p, p, p, p, p, None) == 0   # no tokens: no-op
