@@ -385,10 +385,17 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
     };
     auto pair = [&](int t, auto s0, auto s1) {
       if (t >= n_tiles) return;
+      // The two waves of a SIMD take turns at issue priority, one tile each: left to the
+      // oldest-first default, the first wave runs ahead and then idles at the barrier while its
+      // partner finishes alone (interleaved timings of the long-context causal workload: -0.9%).
+      if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
       compute(t, s0);
       // issued between the two tiles so that they do not compete with tile t's first LDS reads
       if (t + 2 < n_tiles) copy_tile(t + 2);
       if (t + 3 < n_tiles) copy_tile(t + 3);
+      if (wave >= NW / 2) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(1);
       if (t + 1 < n_tiles) compute(t + 1, s1);
       wait_vmcnt0();
       __syncthreads();
