@@ -35,6 +35,14 @@ What is computed, and where it is defined:
 * int8 K/V enter as their dequantized values q * s (one fp32 scale per token)
   -- fkl PR, Summary (compress_kv) and the Verification row that compares the
   int8-KV kernel with an oracle fed the dequantized cache.
+* Score-scope ops (score_epilogue) -- kernbench2 commit page, the tl.composite()
+  epilogue list whose ops each carry a scope: a k_tile op runs on every K tile
+  right after its GEMM, an output_tile op once on the finished tile.  Reading for
+  attention: the K-tile GEMM is the score product, so a score-scope op acts on
+  the raw score x_ij = q_i . k_j of every key (K dequantized, the built-in
+  k_tile dequant of that page's example), in list order, before the softmax
+  scale and the mask: s_ij = sigma * f(x_ij).  A bias op adds vec[j], j the key
+  position in [0, s_k); the epilogue list above is the output_tile scope.
 """
 from __future__ import annotations
 
@@ -73,8 +81,8 @@ def visible_mask(s_q: int, s_k: int, causal: bool, window: int = 0) -> np.ndarra
 
 def apply_epilogue(x: np.ndarray, ops) -> np.ndarray:
     """Apply the post-ops in list order, in fp64.  ops: iterable of (kind, value) with kind
-    "mul" / "add" (scalar value), "bias" (value: a vector over the last axis, the head dim) or
-    "relu" (value ignored; x > 0 ? x : 0).
+    "mul" / "add" (scalar value), "bias" (value: a vector over the last axis -- the head dim of
+    an output row, the key position of a score row) or "relu" (value ignored; x > 0 ? x : 0).
 
     fkl PR, Summary: epilogue=[fkl.Mul(2.0), fkl.Add(0.5)] scales then shifts the output, and
     any compute op may be chained; kernbench2 commit page (the tl.composite epilogue list):
@@ -89,7 +97,7 @@ def apply_epilogue(x: np.ndarray, ops) -> np.ndarray:
         elif kind == "bias":
             b = np.asarray(val, dtype=np.float64)
             if b.shape != y.shape[-1:]:
-                raise ValueError("a bias vector has one value per head-dim channel")
+                raise ValueError("a bias vector has one value per element of the last axis")
             y = y + b
         elif kind == "relu":
             y = np.where(y > 0, y, 0.0)
@@ -99,13 +107,15 @@ def apply_epilogue(x: np.ndarray, ops) -> np.ndarray:
 
 
 def attention(q, k, v, *, causal: bool, window: int = 0, scale: float | None = None,
-              epilogue=(), k_scale=None, v_scale=None, heads=None, rows=None):
+              epilogue=(), k_scale=None, v_scale=None, heads=None, rows=None, score_epilogue=()):
     """Exact attention in fp64.
 
     q: (bh_q, s_q, d); k, v: (bh_kv, s_k, d), any real dtype (int8 when k_scale/v_scale given).
     k_scale, v_scale: (bh_kv, s_k) per-token scales for int8 K/V, or None.
     heads: optional iterable of query-head indices to compute (others left as NaN).
     rows: optional iterable of query-row indices to compute (others left as NaN).
+    score_epilogue: ops applied to the raw scores q.k before the softmax scale (bias: a vector
+    over the s_k keys); epilogue: ops applied to the normalised output rows.
     Returns (out (bh_q, s_q, d) fp64, lse (bh_q, s_q) fp64 natural-log log-sum-exp of the
     scaled scores over visible keys).
     """
@@ -140,7 +150,7 @@ def attention(q, k, v, *, causal: bool, window: int = 0, scale: float | None = N
         qh = q[h].astype(np.float64)
         for r0 in range(0, len(rows), ROW_BLOCK):
             rr = rows[r0:r0 + ROW_BLOCK]
-            s = (qh[rr] @ kh.T) * sm                      # full score rows
+            s = apply_epilogue(qh[rr] @ kh.T, score_epilogue) * sm   # full score rows
             vis = mask_full[rr]
             s = np.where(vis, s, -np.inf)
             mx = s.max(axis=1, keepdims=True)
@@ -159,7 +169,7 @@ def attention(q, k, v, *, causal: bool, window: int = 0, scale: float | None = N
 
 
 def decode(q, k, v, *, window: int = 0, scale: float | None = None, epilogue=(),
-           k_scale=None, v_scale=None, heads=None):
+           k_scale=None, v_scale=None, heads=None, score_epilogue=()):
     """One decode step: each query head has a single row (s_q = 1) that sees every cached key
     (bottom-right alignment), optionally limited to the last `window` keys.
 
@@ -169,7 +179,7 @@ def decode(q, k, v, *, window: int = 0, scale: float | None = None, epilogue=(),
     if q.ndim != 3 or q.shape[1] != 1:
         raise ValueError("decode expects q of shape (bh_q, 1, d)")
     return attention(q, k, v, causal=True, window=window, scale=scale, epilogue=epilogue,
-                     k_scale=k_scale, v_scale=v_scale, heads=heads)
+                     k_scale=k_scale, v_scale=v_scale, heads=heads, score_epilogue=score_epilogue)
 
 
 def merge_lse(o_parts, lse_parts, epilogue=()):

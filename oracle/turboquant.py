@@ -124,12 +124,14 @@ def tq_compression_ratio(d: int, k_bits: int, v_bits: int) -> float:
 
 
 def tq_attention_decode(q, k_packed, k_norms, k_signs, k_bits: int, v_packed, v_norms, v_signs, v_bits: int, *,
-                        k_codebook=None, v_codebook=None, window: int = 0, scale=None, epilogue=()):
+                        k_codebook=None, v_codebook=None, window: int = 0, scale=None, epilogue=(),
+                        score_epilogue=()):
     """Decode attention over a KV cache held as TurboQuant codes: the plain definition, i.e. the
     vectors tq_decode reconstructs from the packed codes and norms, attended by the fp64 decode
     (Foundry attention/ README, TurboQuant section: the coded cache stands in for K and V).
     q (bh_q, 1, d); packed codes (bh_kv, s_k, d bits / 8); norms (bh_kv, s_k); codebooks are the
-    centroid arrays (default: beta_codebook).  Returns (out, lse) as oracle.decode does."""
+    centroid arrays (default: beta_codebook).  score_epilogue acts on the scores against the
+    decoded keys, as in oracle.decode.  Returns (out, lse) as oracle.decode does."""
     from .attention import decode
     kp = np.asarray(k_packed)
     vp = np.asarray(v_packed)
@@ -138,4 +140,4 @@ def tq_attention_decode(q, k_packed, k_norms, k_signs, k_bits: int, v_packed, v_
     vcb = None if v_codebook is None else (np.asarray(v_codebook, np.float64), None)
     kh = tq_decode(tq_unpack(kp, k_bits, d), k_norms, k_signs, k_bits, kcb)
     vh = tq_decode(tq_unpack(vp, v_bits, d), v_norms, v_signs, v_bits, vcb)
-    return decode(q, kh, vh, window=window, scale=scale, epilogue=epilogue)
+    return decode(q, kh, vh, window=window, scale=scale, epilogue=epilogue, score_epilogue=score_epilogue)

@@ -188,6 +188,36 @@ def test_relu_as_abs_or_bias_reversed_is_caught(monkeypatch):
         pin()
 
 
+def test_score_ops_after_the_softmax_scale_are_caught(monkeypatch):
+    """Plant: the score-scope ops act on sigma x instead of x (the oracle then multiplies by sigma
+    again, so the planted form equals f(sigma x))."""
+    from test_oracle_pins import test_score_ops_match_brute_force as pin
+    from test_oracle_pins import TINY
+    case = TINY[3]
+    sig = 1.0 / math.sqrt(case[4])
+    pin(case, 4)
+    orig = oatt.apply_epilogue
+
+    def after_scale(x, ops):
+        if ops and np.ndim(x) == 2 and x.shape[-1] == case[3] and any(kd == "add" for kd, _ in ops):
+            return orig(np.asarray(x) * sig, ops) / sig
+        return orig(x, ops)
+    monkeypatch.setattr(oatt, "apply_epilogue", after_scale)
+    with pytest.raises(AssertionError):
+        pin(case, 4)
+
+
+def test_score_bias_reversed_is_caught(monkeypatch):
+    from test_oracle_pins import test_score_ops_match_brute_force as pin
+    from test_oracle_pins import TINY
+    pin(TINY[2], 3)
+    orig = oatt.apply_epilogue
+    monkeypatch.setattr(oatt, "apply_epilogue",
+                        lambda x, ops: orig(x, [(k, v[::-1]) if k == "bias" else (k, v) for k, v in ops]))
+    with pytest.raises(AssertionError):
+        pin(TINY[2], 3)
+
+
 def _abs_variant(orig, x, ops):
     """The epilogue with relu planted as abs."""
     y = np.array(x, dtype=np.float64)

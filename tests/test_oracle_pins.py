@@ -23,8 +23,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 # ----------------------------------------------------------------------------- brute force
-def brute_attention(q, k, v, causal, window, scale, group, ops=(), ks=None, vs=None):
-    """Pure-Python loops; exact sums via math.fsum.  Independent of numpy linear algebra."""
+def _score_op(x, kind, val, j):
+    """One score-scope op on the raw score x of key j."""
+    if kind == "mul":
+        return x * val
+    if kind == "add":
+        return x + val
+    if kind == "bias":
+        return x + float(val[j])
+    return x if x > 0 else 0.0
+
+
+def brute_attention(q, k, v, causal, window, scale, group, ops=(), ks=None, vs=None, sops=()):
+    """Pure-Python loops; exact sums via math.fsum.  Independent of numpy linear algebra.
+    sops: score-scope ops, applied one key at a time to the raw dot product before the scale."""
     bh_q, s_q, d = len(q), len(q[0]), len(q[0][0])
     s_k = len(k[0])
     out = [[[0.0] * d for _ in range(s_q)] for _ in range(bh_q)]
@@ -43,7 +55,12 @@ def brute_attention(q, k, v, causal, window, scale, group, ops=(), ks=None, vs=N
                 out[h][i] = [0.0] * d
                 lse[h][i] = -math.inf
                 continue
-            sc = {j: scale * math.fsum(float(q[h][i][c]) * kk[j][c] for c in range(d)) for j in keys}
+            sc = {}
+            for j in keys:
+                x = math.fsum(float(q[h][i][c]) * kk[j][c] for c in range(d))
+                for kind, val in sops:
+                    x = _score_op(x, kind, val, j)
+                sc[j] = scale * x
             m = max(sc.values())
             w = {j: math.exp(sc[j] - m) for j in keys}
             z = math.fsum(w.values())
@@ -478,6 +495,100 @@ def test_bias_relu_chain_matches_brute_force():
     o, _ = oracle.attention(q, k, v, causal=True, epilogue=ops)
     assert np.abs(o - o_ref).max() < 1e-13
     assert (o_ref == -0.25).any() and (o_ref > -0.25).any()     # the relu both clipped and passed
+
+
+# ---- score-scope ops (kernbench2 commit page: tl.composite() ops with a k_tile scope run on each
+# K tile right after its GEMM; here, on the raw scores q.k before the softmax scale)
+
+SCORE_CHAINS = [
+    [("mul", 0.5)],
+    [("add", 1.25)],
+    [("relu", None)],
+    [("bias", "vec")],
+    [("mul", 2.0), ("bias", "vec"), ("relu", None), ("add", -0.75)],
+    [("relu", None), ("mul", -1.5)],
+]
+
+
+def _chain(chain, s_k, seed):
+    vec = rng_normal(seed, (s_k,))[0] * 2.0
+    return [(kd, vec.tolist() if vl == "vec" else vl) for kd, vl in chain]
+
+
+@pytest.mark.parametrize("case", TINY[1:6])
+@pytest.mark.parametrize("ci", range(len(SCORE_CHAINS)))
+def test_score_ops_match_brute_force(case, ci):
+    bh_q, bh_kv, s_q, s_k, d, causal, window = case
+    q, k, v = rng_normal(60 + ci, (bh_q, s_q, d), (bh_kv, s_k, d), (bh_kv, s_k, d))
+    sops = _chain(SCORE_CHAINS[ci], s_k, 70 + ci)
+    out_ops = [("mul", 2.0)] if ci % 2 else []
+    scale = 1.0 / math.sqrt(d)
+    o_ref, l_ref = brute_attention(q.tolist(), k.tolist(), v.tolist(), causal, window, scale,
+                                   bh_q // bh_kv, out_ops, sops=sops)
+    o, l = oracle.attention(q, k, v, causal=causal, window=window, epilogue=out_ops, score_epilogue=sops)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-13)
+
+
+def test_score_ops_on_int8_keys_act_on_the_dequantized_score():
+    bh_q, bh_kv, s_q, s_k, d = 4, 2, 3, 7, 4
+    g = np.random.default_rng(77)
+    q = rng_normal(77, (bh_q, s_q, d))[0]
+    kq = g.integers(-127, 128, size=(bh_kv, s_k, d)).astype(np.int8)
+    vq = g.integers(-127, 128, size=(bh_kv, s_k, d)).astype(np.int8)
+    ks = g.uniform(0.001, 0.02, size=(bh_kv, s_k)).astype(np.float32)
+    vs = g.uniform(0.001, 0.02, size=(bh_kv, s_k)).astype(np.float32)
+    sops = _chain(SCORE_CHAINS[4], s_k, 78)
+    o_ref, l_ref = brute_attention(q.tolist(), kq.tolist(), vq.tolist(), True, 0, 0.5, bh_q // bh_kv,
+                                   (), ks.tolist(), vs.tolist(), sops=sops)
+    o, l = oracle.attention(q, kq, vq, causal=True, scale=0.5, k_scale=ks, v_scale=vs, score_epilogue=sops)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-13)
+
+
+def test_score_mul_is_a_softmax_temperature_and_add_shifts_only_the_lse():
+    """Closed forms: sigma * (c x) is the softmax at scale sigma c; sigma (x + c) leaves every
+    probability unchanged and raises the log-sum-exp by sigma c."""
+    q, k, v = rng_normal(81, (4, 9, 16), (2, 13, 16), (2, 13, 16))
+    sig = 0.3
+    o1, l1 = oracle.attention(q, k, v, causal=True, window=5, scale=sig, score_epilogue=[("mul", 1.7)])
+    o2, l2 = oracle.attention(q, k, v, causal=True, window=5, scale=sig * 1.7)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    o3, l3 = oracle.attention(q, k, v, causal=True, window=5, scale=sig, score_epilogue=[("add", -2.5)])
+    o4, l4 = oracle.attention(q, k, v, causal=True, window=5, scale=sig)
+    np.testing.assert_allclose(o3, o4, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l3, l4 - 2.5 * sig, rtol=0, atol=1e-12)
+
+
+def test_score_relu_over_negative_scores_averages_the_visible_values():
+    """With every q.k < 0 a relu makes all scores 0: the output is the plain mean of the visible
+    V rows and the log-sum-exp is log(number of visible keys)."""
+    g = np.random.default_rng(83)
+    q = g.uniform(0.1, 1.0, size=(2, 5, 8))
+    k = -g.uniform(0.1, 1.0, size=(1, 7, 8))
+    v = g.standard_normal((1, 7, 8))
+    o, l = oracle.attention(q, k, v, causal=True, window=3, score_epilogue=[("relu", None)])
+    for i in range(5):
+        ia = i + 2
+        keys = [j for j in range(7) if ia - 3 < j <= ia]
+        for h in range(2):
+            np.testing.assert_allclose(o[h, i], v[0, keys].mean(axis=0), rtol=0, atol=1e-14)
+            assert abs(l[h, i] - math.log(len(keys))) < 1e-14
+
+
+def test_score_bias_of_minus_infinity_size_removes_keys():
+    """A bias far below every score takes its keys out of the softmax exactly (exp underflows to
+    0 in fp64): the result equals attention over the other keys alone."""
+    q, k, v = rng_normal(85, (3, 4, 8), (3, 10, 8), (3, 10, 8))
+    drop = np.array([0, 3, 4, 9])
+    keep = np.setdiff1d(np.arange(10), drop)
+    bias = np.zeros(10)
+    bias[drop] = -1e6
+    o1, l1 = oracle.attention(q, k, v, causal=False, score_epilogue=[("bias", bias)])
+    o2, l2 = oracle.attention(q, k[:, keep], v[:, keep], causal=False)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
 
 
 # ---- rotate-half RoPE in the cache write (FlashRT QKV Cache RoPE: the decode K write)
