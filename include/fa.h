@@ -78,12 +78,30 @@ typedef enum { FA_EPI_MUL = 1, FA_EPI_ADD = 2, FA_EPI_BIAS = 3, FA_EPI_RELU = 4 
  *   FA_EPI_BIAS  x + vec[c], c the head-dim index of the element; vec is a device fp32 array
  *                of head_dim values (4-byte aligned), required for this kind and NULL otherwise
  *   FA_EPI_RELU  x > 0 ? x : +0 (value unused)
- * Values, vectors and the list itself are kernel arguments: changing any of them never selects
- * another kernel (fkl PR, Verification: epilogue values change without recompile). */
+ * Every op carries a scope (kernbench2 commit page, the same commit: each tl.composite() op is
+ * flagged output_tile, the default, k_tile, run on every K tile right after its GEMM, or kernel):
+ *   FA_SCOPE_OUTPUT_TILE  (0, so a zero-initialised op keeps the behaviour above) the normalised
+ *                         output row, as described above.
+ *   FA_SCOPE_K_TILE       every raw score x = q.k_j of a key tile (K dequantized), before the
+ *                         mask and the softmax scale: the softmax then sees scale * f(x).  For
+ *                         FA_EPI_BIAS, vec[j] is added, j the key position in [0, s_k): vec is a
+ *                         device fp32 array of s_k values shared by all heads.  Accepted by
+ *                         fa_forward, fa_decode, fa_decode_noalloc and fa_tq_attention_decode;
+ *                         fa_merge_lse, which forms no scores, returns FA_ERR_UNSUPPORTED.
+ *   FA_SCOPE_KERNEL       FA_ERR_UNSUPPORTED: no step of attention runs once per kernel.
+ * The ops of each scope run in their list order; both scopes together hold at most
+ * FA_MAX_EPILOGUE ops.  Values, vectors and the list itself are kernel arguments: changing them
+ * never selects another kernel (fkl PR, Verification: epilogue values change without
+ * recompile); only whether any K-tile op is present does (an instantiation whose
+ * fa_last_kernel name ends in "_sops"). */
+typedef enum { FA_SCOPE_OUTPUT_TILE = 0, FA_SCOPE_K_TILE = 1, FA_SCOPE_KERNEL = 2 } fa_epi_scope;
+
 typedef struct {
   int32_t kind;        /* fa_epi_kind */
   float value;         /* FA_EPI_MUL / FA_EPI_ADD */
-  const float* vec;    /* FA_EPI_BIAS: device [head_dim]; NULL for the other kinds */
+  const float* vec;    /* FA_EPI_BIAS: device [head_dim] (output scope) or [s_k] (K-tile scope);
+                          NULL for the other kinds */
+  int32_t scope;       /* fa_epi_scope */
 } fa_epilogue_op;
 
 #define FA_MAX_EPILOGUE 8

@@ -59,7 +59,8 @@ class Add:
 
 @dataclass(frozen=True, eq=False)
 class Bias:
-    """Epilogue op: out[..., c] = out[..., c] + vec[c] for a device fp32 vector of head_dim values."""
+    """Epilogue op: out[..., c] = out[..., c] + vec[c] for a device fp32 vector of head_dim values;
+    as a score op, score[j] + vec[j] for a vector of s_k values (one per key position)."""
     vec: object
 
 
@@ -69,7 +70,11 @@ class ReLU:
 
 
 class _EpiOp(ctypes.Structure):
-    _fields_ = [("kind", ctypes.c_int32), ("value", ctypes.c_float), ("vec", ctypes.c_void_p)]
+    _fields_ = [("kind", ctypes.c_int32), ("value", ctypes.c_float), ("vec", ctypes.c_void_p),
+                ("scope", ctypes.c_int32)]
+
+
+_SCOPE_OUTPUT_TILE, _SCOPE_K_TILE = 0, 1
 
 
 _lib = None
@@ -198,29 +203,35 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def _epilogue(ops, head_dim=None):
+def _epilogue(ops, head_dim=None, score_ops=(), s_k=None):
+    """Op array for the C ABI: `ops` on the output rows (a Bias has head_dim values), then
+    `score_ops` on the raw scores q.k before the softmax scale (a Bias has s_k values, one per
+    key position)."""
     ops = list(ops or [])
-    if len(ops) > _MAX_EPI:
-        raise ValueError(f"at most {_MAX_EPI} epilogue ops")
-    arr = (_EpiOp * max(1, len(ops)))()
-    for i, op in enumerate(ops):
+    score_ops = list(score_ops or [])
+    if len(ops) + len(score_ops) > _MAX_EPI:
+        raise ValueError(f"at most {_MAX_EPI} epilogue ops in all")
+    arr = (_EpiOp * max(1, len(ops) + len(score_ops)))()
+    tagged = [(op, _SCOPE_OUTPUT_TILE, head_dim, "head_dim") for op in ops]
+    tagged += [(op, _SCOPE_K_TILE, s_k, "s_k") for op in score_ops]
+    for i, (op, scope, n_vec, what) in enumerate(tagged):
         if isinstance(op, Mul):
-            arr[i] = _EpiOp(_EPI_MUL, float(op.value), None)
+            arr[i] = _EpiOp(_EPI_MUL, float(op.value), None, scope)
         elif isinstance(op, Add):
-            arr[i] = _EpiOp(_EPI_ADD, float(op.value), None)
+            arr[i] = _EpiOp(_EPI_ADD, float(op.value), None, scope)
         elif isinstance(op, Bias):
             torch = _torch()
             vec = op.vec
             if not isinstance(vec, torch.Tensor) or vec.dtype != torch.float32 or vec.dim() != 1:
                 raise ValueError("Bias needs a 1-D fp32 device tensor")
-            if head_dim is not None and vec.numel() != head_dim:
-                raise ValueError(f"Bias vector has {vec.numel()} values, head_dim is {head_dim}")
-            arr[i] = _EpiOp(_EPI_BIAS, 0.0, _dev(vec, "bias vector"))
+            if n_vec is not None and vec.numel() != n_vec:
+                raise ValueError(f"Bias vector has {vec.numel()} values, {what} is {n_vec}")
+            arr[i] = _EpiOp(_EPI_BIAS, 0.0, _dev(vec, "bias vector"), scope)
         elif isinstance(op, ReLU):
-            arr[i] = _EpiOp(_EPI_RELU, 0.0, None)
+            arr[i] = _EpiOp(_EPI_RELU, 0.0, None, scope)
         else:
             raise TypeError(f"epilogue ops must be Mul, Add, Bias or ReLU, got {op!r}")
-    return arr, len(ops)
+    return arr, len(tagged)
 
 
 def compress_kv(x, out=None, scales=None):
@@ -280,10 +291,12 @@ def append_kv(k_new, v_new, pos, k_cache, v_cache, k_scale, v_scale, rope_cos=No
 
 
 def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(), k_scale=None,
-                    v_scale=None, out_dtype=None, out=None, return_lse=False):
+                    v_scale=None, out_dtype=None, out=None, return_lse=False, score_ops=()):
     """softmax(Q K^T * scale) V for q (bh_q, s_q, d) over k, v (bh_kv, s_k, d).
 
     k, v: fp32 / bf16 tensors, or int8 codes with k_scale, v_scale (bh_kv, s_k) fp32.
+    epilogue: ops on the normalised output; score_ops: ops on every raw score q.k before the
+    softmax scale (a Bias there holds s_k values, one per key position).
     out_dtype defaults to q's dtype.  Returns out, or (out, lse) with return_lse.
     """
     torch = _torch()
@@ -309,7 +322,7 @@ def flash_attention(q, k, v, *, causal=False, window=0, scale=None, epilogue=(),
         raise ValueError(f"out must have shape {(bh_q, s_q, d)}, got {tuple(out.shape)}")
     _same_device(q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out)
     lse = torch.empty((bh_q, s_q), dtype=torch.float32, device=q.device) if return_lse else None
-    epi, n_epi = _epilogue(epilogue, d)
+    epi, n_epi = _epilogue(epilogue, d, score_ops, s_k)
     _check(lib().fa_forward(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dtype_code(k),
                             _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _dev(out, "out"),
                             _out_code(out.dtype), _dev(lse, "lse"), bh_q, bh_kv, s_q, s_k, d,
@@ -415,9 +428,10 @@ def decode_workspace_bytes(bh_q, bh_kv, s_k, head_dim, num_splits=0) -> int:
 
 
 def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epilogue=(),
-           out_dtype=None, out=None, workspace=None, return_lse=False):
+           out_dtype=None, out=None, workspace=None, return_lse=False, score_ops=()):
     """One decode step: q (bh_q, 1, d) against the int8 cache k, v (bh_kv, s_k, d) with fp32
-    per-token scales (bh_kv, s_k).  Output fp32 by default."""
+    per-token scales (bh_kv, s_k).  score_ops act on the raw scores as in flash_attention.
+    Output fp32 by default."""
     torch = _torch()
     if q.dim() != 3 or q.shape[1] != 1:
         raise ValueError("q must have shape (bh_q, 1, head_dim)")
@@ -439,7 +453,7 @@ def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epi
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     lse = torch.empty((bh_q,), dtype=torch.float32, device=q.device) if return_lse else None
-    epi, n_epi = _epilogue(epilogue, d)
+    epi, n_epi = _epilogue(epilogue, d, score_ops, s_k)
     _check(lib().fa_decode(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dev(k_scale, "k_scale"),
                            _dev(v_scale, "v_scale"), _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"),
                            bh_q, bh_kv, s_k, d, float(scale) if scale else 0.0, int(window), int(num_splits),
@@ -448,7 +462,8 @@ def decode(q, k, v, k_scale, v_scale, *, window=0, scale=None, num_splits=0, epi
     return (out, lse) if return_lse else out
 
 
-def decode_noalloc(q, k, v, k_scale, v_scale, out, *, lse=None, window=0, scale=None, num_splits=0, epilogue=()):
+def decode_noalloc(q, k, v, k_scale, v_scale, out, *, lse=None, window=0, scale=None, num_splits=0, epilogue=(),
+                   score_ops=()):
     """decode() through fa_decode_noalloc: the partial states go to the library's fixed device
     scratch array, and nothing is allocated here either, so the caller passes `out` (bh_q, 1, d)
     (and optionally `lse` (bh_q,) fp32).  Calls that may overlap on one GPU race on that array."""
@@ -468,7 +483,7 @@ def decode_noalloc(q, k, v, k_scale, v_scale, out, *, lse=None, window=0, scale=
     if lse is not None:
         _want(lse, "lse", (bh_q,), torch.float32)
     _same_device(q, k=k, v=v, k_scale=k_scale, v_scale=v_scale, out=out, lse=lse)
-    epi, n_epi = _epilogue(epilogue, d)
+    epi, n_epi = _epilogue(epilogue, d, score_ops, s_k)
     _check(lib().fa_decode_noalloc(_dev(q, "q"), _dtype_code(q), _dev(k, "k"), _dev(v, "v"), _dev(k_scale, "k_scale"),
                                    _dev(v_scale, "v_scale"), _dev(out, "out"), _out_code(out.dtype), _dev(lse, "lse"),
                                    bh_q, bh_kv, s_k, d, float(scale) if scale else 0.0, int(window), int(num_splits),
@@ -478,10 +493,11 @@ def decode_noalloc(q, k, v, k_scale, v_scale, out, *, lse=None, window=0, scale=
 
 def tq_attention_decode(q, k_codes, k_norms, k_signs, k_bits, k_codebook, v_codes, v_norms, v_signs, v_bits,
                         v_codebook, *, window=0, scale=None, num_splits=0, epilogue=(), out_dtype=None, out=None,
-                        workspace=None, return_lse=False):
+                        workspace=None, return_lse=False, score_ops=()):
     """One decode step of q (bh_q, 1, d) over a KV cache held as TurboQuant codes: k_codes
     (bh_kv, s_k, d k_bits / 8) uint8 with k_norms (bh_kv, s_k) fp32 and k_signs (d,) int8 as
-    tq_encode wrote them, k_codebook the host centroids; likewise for V.  Output fp32 by default."""
+    tq_encode wrote them, k_codebook the host centroids; likewise for V.  score_ops act on the
+    scores n_j (q'.c[code]) before the softmax scale, as in flash_attention.  Output fp32 by default."""
     torch = _torch()
     if q.dim() != 3 or q.shape[1] != 1:
         raise ValueError("q must have shape (bh_q, 1, head_dim)")
@@ -509,7 +525,7 @@ def tq_attention_decode(q, k_codes, k_norms, k_signs, k_bits, k_codebook, v_code
     lse = torch.empty((bh_q,), dtype=torch.float32, device=q.device) if return_lse else None
     kcb, kcbp = _host_f32(k_codebook)
     vcb, vcbp = _host_f32(v_codebook)
-    epi, n_epi = _epilogue(epilogue, d)
+    epi, n_epi = _epilogue(epilogue, d, score_ops, s_k)
     _check(L.fa_tq_attention_decode(_dev(q, "q"), _dtype_code(q), _dev(k_codes, "k_codes"), _dev(k_norms, "k_norms"),
                                     _dev(k_signs, "k_signs"), int(k_bits), kcbp, _dev(v_codes, "v_codes"),
                                     _dev(v_norms, "v_norms"), _dev(v_signs, "v_signs"), int(v_bits), vcbp,

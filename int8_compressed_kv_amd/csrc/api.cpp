@@ -43,8 +43,11 @@ int check_head_dim(int32_t d) {
   return FA_OK;
 }
 
-int fill_epilogue(const fa_epilogue_op* epi, int32_t n_epi, fa::EpiArgs* out) {
+// Splits the op list by scope: output-tile ops into *out, K-tile (score) ops into *sops, or an
+// error when sops is null (a call that forms no scores).
+int fill_epilogue(const fa_epilogue_op* epi, int32_t n_epi, fa::EpiArgs* out, fa::EpiArgs* sops) {
   std::memset(out, 0, sizeof(*out));
+  if (sops) std::memset(sops, 0, sizeof(*sops));
   if (n_epi < 0) return fail(FA_ERR_INVALID, "n_epi must be >= 0 (got %d)", n_epi);
   if (n_epi > FA_MAX_EPILOGUE)
     return fail(FA_ERR_UNSUPPORTED, "at most %d epilogue ops are supported (got %d)", FA_MAX_EPILOGUE, n_epi);
@@ -57,11 +60,19 @@ int fill_epilogue(const fa_epilogue_op* epi, int32_t n_epi, fa::EpiArgs* out) {
       return fail(FA_ERR_INVALID, "epilogue op %d (bias) needs a 4-byte aligned device vector", i);
     if (k != FA_EPI_BIAS && epi[i].vec)
       return fail(FA_ERR_INVALID, "epilogue op %d: vec must be NULL unless the kind is FA_EPI_BIAS", i);
-    out->kind[i] = k;
-    out->value[i] = epi[i].value;
-    out->vec[i] = epi[i].vec;
+    const int sc = epi[i].scope;
+    if (sc != FA_SCOPE_OUTPUT_TILE && sc != FA_SCOPE_K_TILE && sc != FA_SCOPE_KERNEL)
+      return fail(FA_ERR_INVALID, "epilogue op %d has unknown scope %d", i, sc);
+    if (sc == FA_SCOPE_KERNEL)
+      return fail(FA_ERR_UNSUPPORTED, "epilogue op %d: the kernel scope is not supported", i);
+    if (sc == FA_SCOPE_K_TILE && !sops)
+      return fail(FA_ERR_UNSUPPORTED, "epilogue op %d: K-tile ops need a call that forms scores", i);
+    fa::EpiArgs* dst = sc == FA_SCOPE_K_TILE ? sops : out;
+    dst->kind[dst->n] = k;
+    dst->value[dst->n] = epi[i].value;
+    dst->vec[dst->n] = epi[i].vec;
+    ++dst->n;
   }
-  out->n = n_epi;
   return FA_OK;
 }
 
@@ -201,8 +212,8 @@ int fa_forward(const void* q, int32_t q_dtype, const void* k, const void* v, int
   } else if (k_scale || v_scale) {
     return fail(FA_ERR_INVALID, "k_scale/v_scale must be NULL unless kv dtype is FA_I8");
   }
-  fa::EpiArgs ea;
-  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  fa::EpiArgs ea, sa;
+  if (int r = fill_epilogue(epi, n_epi, &ea, &sa)) return r;
   if (s_q == 0) return FA_OK;
   if (!q || !out) return fail(FA_ERR_INVALID, "null q or out");
   if (s_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "null k or v");
@@ -232,6 +243,7 @@ int fa_forward(const void* q, int32_t q_dtype, const void* k, const void* v, int
   a.scale = resolve_scale(softmax_scale, head_dim);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.epi = ea;
+  a.sops = sa;
   const char* name = "";
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = f32_path              ? fa::launch_prefill_f32(a, head_dim, kv_dtype, st, &name)
@@ -251,7 +263,7 @@ int fa_merge_lse(const float* o_parts, const float* lse_parts, int32_t n_parts, 
   if (rows < 0) return fail(FA_ERR_INVALID, "rows must be >= 0");
   if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "out dtype must be FA_F32 or FA_BF16");
   fa::EpiArgs ea;
-  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  if (int r = fill_epilogue(epi, n_epi, &ea, nullptr)) return r;
   if (rows == 0) return FA_OK;
   if (!o_parts || !lse_parts || !out) return fail(FA_ERR_INVALID, "null pointer argument");
   if (!aligned16(o_parts) || !aligned16(out) || (reinterpret_cast<uintptr_t>(lse_parts) & 3u) ||
@@ -395,8 +407,8 @@ int decode_impl(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v
   if (out_dtype != FA_F32 && out_dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "decode out must be FA_F32 or FA_BF16");
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(FA_ERR_INVALID, "num_splits must be in [0, %d] (got %d)", kMaxSplits, num_splits);
-  fa::EpiArgs ea;
-  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  fa::EpiArgs ea, sa;
+  if (int r = fill_epilogue(epi, n_epi, &ea, &sa)) return r;
   if (!q || !out) return fail(FA_ERR_INVALID, "null q or out");
   if (s_k > 0 && (!k || !v || !k_scale || !v_scale)) return fail(FA_ERR_INVALID, "null k, v or scales");
   if (!aligned16(q) || !aligned16(out) || (s_k > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(k_scale) ||
@@ -448,6 +460,7 @@ int decode_impl(const void* q, int32_t q_dtype, const int8_t* k, const int8_t* v
   a.scale = resolve_scale(softmax_scale, head_dim);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.epi = ea;
+  a.sops = sa;
   const char* name = "";
   hipError_t e = fa::launch_decode(a, head_dim, st, &name);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -522,8 +535,8 @@ int fa_tq_attention_decode(const void* q, int32_t q_dtype, const uint8_t* k_code
     return fail(FA_ERR_INVALID, "num_splits must be in [0, %d] (got %d)", kMaxSplits, num_splits);
   if (int r = check_codebook(k_codebook, k_bits)) return r;
   if (int r = check_codebook(v_codebook, v_bits)) return r;
-  fa::EpiArgs ea;
-  if (int r = fill_epilogue(epi, n_epi, &ea)) return r;
+  fa::EpiArgs ea, sa;
+  if (int r = fill_epilogue(epi, n_epi, &ea, &sa)) return r;
   if (!q || !out || !k_signs || !v_signs) return fail(FA_ERR_INVALID, "null q, out or signs");
   if (s_k > 0 && (!k_codes || !v_codes || !k_norms || !v_norms)) return fail(FA_ERR_INVALID, "null codes or norms");
   if (!aligned16(q) || !aligned16(out) || (s_k > 0 && (!aligned16(k_codes) || !aligned16(v_codes))))
@@ -564,6 +577,7 @@ int fa_tq_attention_decode(const void* q, int32_t q_dtype, const uint8_t* k_code
   a.k_e = codebook_digits(k_codebook, k_bits, a.ktab);
   a.v_e = codebook_digits(v_codebook, v_bits, a.vtab);
   a.epi = ea;
+  a.sops = sa;
   const char* name = "";
   hipError_t e = fa::launch_tq_attention(a, head_dim, k_bits, v_bits, static_cast<hipStream_t>(stream), &name);
   if (e != hipSuccess) return hip_fail(e, "TurboQuant attention launch");

@@ -101,7 +101,7 @@ __device__ __forceinline__ int dswz(int r) {
   return ((r >> 1) ^ (r >> 4)) & (SP - 1);
 }
 
-template <int D, int NS>
+template <int D, int NS, bool SOPS>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeArgs a) {
   using C = DCfg<D>;
   constexpr int KT = C::KT, NC16 = C::NC16, SP = C::SP, VCH = C::VCH;
@@ -345,6 +345,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
           s[kb][v] = y * ks[kb][v];
         }
       }
+      if constexpr (SOPS) {
+        float x[KB * 4];
+#pragma unroll
+        for (int j = 0; j < KB * 4; ++j) x[j] = s[j / 4][j % 4];
+        apply_score_ops(x, a.sops, [&](int j) { return min(k0 + KG * hq + j, last_key); });
+#pragma unroll
+        for (int j = 0; j < KB * 4; ++j) s[j / 4][j % 4] = x[j];
+      }
       if (tail) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -548,11 +556,14 @@ hipError_t launch_d(const DecodeArgs& a_in, hipStream_t st, const char** name) {
   a.tiles_per_split = (tiles + a.num_splits - 1) / a.num_splits;
   const int hpw = 4 * NS;
   const dim3 grid((unsigned)a.num_splits, (unsigned)a.bh_kv, (unsigned)((a.group + hpw - 1) / hpw));
-  hipLaunchKernelGGL((decode_partial_kernel<D, NS>), grid, dim3(64 * kWaves), 0, st, a);
+  const bool so = a.sops.n > 0;
+  if (so) hipLaunchKernelGGL((decode_partial_kernel<D, NS, true>), grid, dim3(64 * kWaves), 0, st, a);
+  else hipLaunchKernelGGL((decode_partial_kernel<D, NS, false>), grid, dim3(64 * kWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.bh_q), dim3(64), 0, st, a);
-  *name = NS == 2 ? "decode_int8_h8" : "decode_int8";
+  if (NS == 2) *name = so ? "decode_int8_h8_sops" : "decode_int8_h8";
+  else *name = so ? "decode_int8_sops" : "decode_int8";
   return hipGetLastError();
 }
 

@@ -164,6 +164,14 @@ __device__ __forceinline__ void apply_epilogue_all(float (&x)[N], const EpiArgs&
   }
 }
 
+// Score-scope ops over a tile's raw scores x[j] = q.k, before the mask and the softmax scale;
+// key(j) is the key position of x[j], which the caller clamps into [0, s_k) so that a bias read
+// stays inside its vector (scores of keys past the end are masked right after).
+template <int N, class Key>
+__device__ __forceinline__ void apply_score_ops(float (&x)[N], const EpiArgs& e, Key key) {
+  apply_epilogue_all(x, e, key);
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
 }  // namespace fa

@@ -13,11 +13,14 @@ constexpr int kEpiAdd = 2;
 constexpr int kEpiBias = 3;   // + vec[channel]
 constexpr int kEpiRelu = 4;   // max(x, +0)
 
+// An op list of one scope.  Output scope (`epi`): ops on the normalised output row, a bias
+// indexed by head-dim channel.  Score scope (`sops`): ops on every raw score q.k of a key tile
+// before the mask and the softmax scale, a bias indexed by key position.
 struct EpiArgs {
   int32_t n;
   int32_t kind[kMaxEpilogue];
   float value[kMaxEpilogue];
-  const float* vec[kMaxEpilogue];   // per-channel vector of a bias op, else null
+  const float* vec[kMaxEpilogue];   // vector of a bias op, else null
 };
 
 enum DType : int32_t { kF32 = 0, kBF16 = 1, kI8 = 2 };
@@ -37,6 +40,7 @@ struct PrefillArgs {
   float scale;          // softmax scale sigma
   float scale_log2;     // sigma * log2(e)
   EpiArgs epi;
+  EpiArgs sops;         // score-scope ops (the kernel instantiation with them runs only when n > 0)
 };
 
 struct DecodeArgs {
@@ -56,6 +60,7 @@ struct DecodeArgs {
   int32_t q_bf16, out_bf16;
   float scale, scale_log2;
   EpiArgs epi;
+  EpiArgs sops;         // score-scope ops
 };
 
 struct AppendArgs {
@@ -115,6 +120,7 @@ struct TqAttnArgs {
   uint32_t vtab[3][4];
   int32_t k_e, v_e;
   EpiArgs epi;
+  EpiArgs sops;           // score-scope ops, on n_j (q'.c[code]) before the softmax scale
 };
 
 // Query heads one decode workgroup serves: 8 (two MFMA column sets) for groups of more than 4

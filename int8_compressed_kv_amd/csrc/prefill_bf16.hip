@@ -81,7 +81,7 @@ __device__ __forceinline__ void wait_vmcnt0() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
+template <int D, bool SOPS>
 __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(PrefillArgs a) {
   using C = Cfg<D>;
   constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, CH = C::CH;
@@ -263,6 +263,19 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       // V^T fragments of the first 32 keys, read while the softmax runs
       u32x4 vf0[2][NDB];
       vread(Vt, 0, vf0);
+
+      if constexpr (SOPS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int kl0 = k0 + 32 * kb + 4 * h;
+          float x[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = S[kb][i];
+          apply_score_ops(x, a.sops, [&](int i) { return min(kl0 + 8 * (i / 4) + (i % 4), a.s_k - 1); });
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[kb][i] = x[i];
+        }
+      }
 
       if (need_mask) {
         // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
@@ -471,8 +484,13 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t st, const char** name) {
   const int64_t n_qb = (a.s_q + Cfg<D>::BM - 1) / Cfg<D>::BM;
   const int64_t blocks = n_qb * a.bh_q;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
-  *name = "prefill_bf16";
+  if (a.sops.n > 0) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
+    *name = "prefill_bf16_sops";
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
+    *name = "prefill_bf16";
+  }
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@
 namespace fa {
 namespace {
 
-template <int D, bool KV_I8>
+template <int D, bool KV_I8, bool SOPS>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   constexpr int BM = 32;
   constexpr int BN = 32;
@@ -129,6 +129,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       const int j = k0 + kl;
       float s = S[i];
       if (KV_I8) s *= kss[kl];
+      if constexpr (SOPS) s = apply_epilogue(s, a.sops, min(j, a.s_k - 1));
       bool vis = j < a.s_k;
       if (a.causal) vis = vis && (j <= qi + off);
       if (a.window) vis = vis && (j > qi + off - a.window);
@@ -196,12 +197,15 @@ template <int D>
 hipError_t launch_d(const PrefillArgs& a, int32_t kv_dtype, hipStream_t st, const char** name) {
   const int n_qb = (a.s_q + 31) / 32;
   const dim3 grid((unsigned)(n_qb * a.bh_q));
+  const bool so = a.sops.n > 0;
   if (kv_dtype == kI8) {
-    hipLaunchKernelGGL((prefill_f32_kernel<D, true>), grid, dim3(64), 0, st, a);
-    *name = "prefill_f32_i8kv";
+    if (so) hipLaunchKernelGGL((prefill_f32_kernel<D, true, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((prefill_f32_kernel<D, true, false>), grid, dim3(64), 0, st, a);
+    *name = so ? "prefill_f32_i8kv_sops" : "prefill_f32_i8kv";
   } else {
-    hipLaunchKernelGGL((prefill_f32_kernel<D, false>), grid, dim3(64), 0, st, a);
-    *name = "prefill_f32";
+    if (so) hipLaunchKernelGGL((prefill_f32_kernel<D, false, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((prefill_f32_kernel<D, false, false>), grid, dim3(64), 0, st, a);
+    *name = so ? "prefill_f32_sops" : "prefill_f32";
   }
   return hipGetLastError();
 }

@@ -90,7 +90,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
+template <int D, bool SOPS>
 __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(PrefillArgs a) {
   using C = Cfg<D>;
   constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, CH = C::CH;
@@ -296,6 +296,20 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     // V^T fragments of the first 32 keys, read while the softmax runs
     u32x4 vf0[2][NDB];
     vread(Vt, 0, vf0);
+
+    if constexpr (SOPS) {
+      // the ops act on S = S~ 2^es (exact power-of-two rescalings either way)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kl0 = k0 + 32 * kb + 4 * h;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = ldexpf(S[kb][i], es);
+        apply_score_ops(x, a.sops, [&](int i) { return min(kl0 + 8 * (i / 4) + (i % 4), last_key); });
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb][i] = ldexpf(x[i], -es);
+      }
+    }
 
     if (need_mask) {
       // key offset of element i is 8 (i/4) + i%4 past kl0; visible iff lo_i <= it <= hi_i
@@ -598,8 +612,11 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t st, const char** name) {
   const int64_t n_qb = (a.s_q + Cfg<D>::BM - 1) / Cfg<D>::BM;
   const int64_t blocks = n_qb * a.bh_q;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_i8kv_kernel<D>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
-  *name = "prefill_bf16_i8kv";
+  if (a.sops.n > 0)
+    hipLaunchKernelGGL((prefill_i8kv_kernel<D, true>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_i8kv_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * Cfg<D>::NW), 0, st, a);
+  *name = a.sops.n > 0 ? "prefill_bf16_i8kv_sops" : "prefill_bf16_i8kv";
   return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ __device__ __forceinline__ int k_slot_channel(int kk, int hq, int s) {
   else return base + 4 * e + w;
 }
 
-template <int D, int KBITS, int VBITS>
+template <int D, int KBITS, int VBITS, bool SOPS>
 __global__ __launch_bounds__(64 * kTqWaves, (D == 128 && KBITS == 4 && VBITS == 4) ? 1 : 2)   // 4/4 needs > 256 VGPRs
 void tq_attn_partial_kernel(TqAttnArgs a) {
   using C = TqCfg<D, KBITS, VBITS>;
@@ -346,6 +346,14 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
         s[kb][v] = y * kn[v];
       }
     }
+    if constexpr (SOPS) {
+      float x[NKB * 4];
+#pragma unroll
+      for (int j = 0; j < NKB * 4; ++j) x[j] = s[j / 4][j % 4];
+      apply_score_ops(x, a.sops, [&](int j) { return min(k0 + KG * hq + j, last_key); });
+#pragma unroll
+      for (int j = 0; j < NKB * 4; ++j) s[j / 4][j % 4] = x[j];
+    }
     if (tail) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -558,11 +566,13 @@ hipError_t launch_tq_attn_d(const TqAttnArgs& a_in, hipStream_t st, const char**
   const int tiles = (a.s_k - a.key_lo + KT - 1) / KT;
   a.tiles_per_split = (tiles + a.num_splits - 1) / a.num_splits;
   const dim3 grid((unsigned)a.num_splits, (unsigned)a.bh_kv, (unsigned)((a.group + 3) / 4));
-  hipLaunchKernelGGL((tq_attn_partial_kernel<D, KB, VB>), grid, dim3(64 * kTqWaves), 0, st, a);
+  const bool so = a.sops.n > 0;
+  if (so) hipLaunchKernelGGL((tq_attn_partial_kernel<D, KB, VB, true>), grid, dim3(64 * kTqWaves), 0, st, a);
+  else hipLaunchKernelGGL((tq_attn_partial_kernel<D, KB, VB, false>), grid, dim3(64 * kTqWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((tq_attn_merge_kernel<D>), dim3((unsigned)a.bh_q), dim3(64), 0, st, a);
-  *name = "tq_attention_decode";
+  *name = so ? "tq_attention_decode_sops" : "tq_attention_decode";
   return hipGetLastError();
 }
 

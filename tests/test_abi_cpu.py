@@ -189,7 +189,25 @@ def test_bias_and_relu_ops_are_validated_on_host(L):
     assert _fwd(L, epi=odd_vec, n_epi=1) == -1
     stray_vec = (E * 1)(E(4, 0.0, 1 << 20))
     assert _fwd(L, epi=stray_vec, n_epi=1) == -1 and "NULL" in fa.last_error()
-    assert ctypes.sizeof(E) == 16   # int32 kind, float value, pointer vec
+    assert ctypes.sizeof(E) == 24   # int32 kind, float value, pointer vec, int32 scope (+ padding)
+
+
+def test_epilogue_scopes_are_validated_on_host(L):
+    E = fa._EpiOp
+    # K-tile (score) ops are accepted by the calls that form scores ...
+    both = (E * 3)(E(1, 2.0, None, 0), E(3, 0.0, 1 << 20, 1), E(4, 0.0, None, 1))
+    assert _fwd(L, epi=both, n_epi=3, q=0) == -1 and "null q" in fa.last_error()
+    assert _dec(L, epi=both, n_epi=3, q=0) == -1 and "null" in fa.last_error()
+    # ... and refused by the merge, which forms none
+    assert _mrg(L, epi=both, n_epi=3) == -2 and "K-tile" in fa.last_error()
+    out_only = (E * 1)(E(1, 2.0, None, 0))
+    assert _mrg(L, epi=out_only, n_epi=1, o=0) == -1 and "null" in fa.last_error()
+    kernel = (E * 1)(E(1, 2.0, None, 2))
+    assert _fwd(L, epi=kernel, n_epi=1) == -2 and "kernel scope" in fa.last_error()
+    bad = (E * 1)(E(1, 2.0, None, 5))
+    assert _fwd(L, epi=bad, n_epi=1) == -1 and "scope" in fa.last_error()
+    nine = (E * 9)(*[E(1, 1.0, None, i % 2) for i in range(9)])
+    assert _fwd(L, epi=nine, n_epi=9) == -2
 
 
 def test_python_epilogue_ops_check_the_bias_vector():
@@ -200,6 +218,12 @@ def test_python_epilogue_ops_check_the_bias_vector():
         fa._epilogue([fa.Bias(torch.zeros(32))], 64)
     arr, n = fa._epilogue([fa.ReLU(), fa.Mul(2.0)], 64)
     assert n == 2 and arr[0].kind == 4 and arr[1].kind == 1
+    arr, n = fa._epilogue([fa.Mul(2.0)], 64, [fa.Add(1.0), fa.ReLU()], 1000)
+    assert n == 3 and [arr[i].scope for i in range(3)] == [0, 1, 1] and arr[1].kind == 2
+    with pytest.raises(ValueError):       # a score bias holds s_k values
+        fa._epilogue([], 64, [fa.Bias(torch.zeros(64))], 1000)
+    with pytest.raises(ValueError):
+        fa._epilogue([fa.Mul(1.0)] * 5, 64, [fa.Mul(1.0)] * 4, 1000)
 
 
 def test_tq_codebook_on_host_matches_the_oracle_in_fp32(L):
