@@ -97,6 +97,7 @@ struct TqArgs {
   float inv_sqrt_d;
   float thr[15];          // encode: the 2^bits - 1 thresholds, ascending
   float cb[16];           // decode: the 2^bits centroids, ascending
+  uint32_t tab[128][2];   // 4-bit encode: decision table by (sign, bucket of |u|), filled by the launcher
 };
 
 struct TqAttnArgs {

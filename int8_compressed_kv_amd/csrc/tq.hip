@@ -58,6 +58,49 @@ __device__ __forceinline__ void cross_stage(float (&v)[16], int sl) {
   }
 }
 
+// The same butterfly over quad lanes (X = 1, 2) as one DPP multiply-add per value: v = partner * g
+// + own gives a + b on the lower lane and b - a = -(a - b) on the upper, so the upper lane's values
+// come out negated.  After stages over the lane bits in `done`, a lane's values carry the sign
+// (-1)^popcount(sl & done), the same for all 16 of them (partners of a later stage agree in the
+// bits already done); the caller folds that sign into its per-lane scale.
+template <int X, int SEG>
+__device__ __forceinline__ void cross_stage_signed(float (&v)[16], int sl) {
+  static_assert(X <= 2, "quad-lane stages only");
+  if constexpr (X < SEG) {
+    const float g = (sl & X) ? -1.f : 1.f;
+    // v_fmac_f32 with its src0 read from the partner lane (DPP quad permute): the compiler does not
+    // fold a DPP move into a multiply-accumulate, so the 16 are written out.  s_nop 1: the DPP read
+    // of a VGPR must trail the VALU write of it by two wait states; inside the block no instruction
+    // reads a register another one writes.
+#define FA_DPP_FMAC(i) "v_fmac_f32_dpp %" #i ", %" #i ", %16 " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+#define FA_DPP_BLOCK                                                                                  \
+  asm("s_nop 1\n" FA_DPP_FMAC(0) FA_DPP_FMAC(1) FA_DPP_FMAC(2) FA_DPP_FMAC(3) FA_DPP_FMAC(4) FA_DPP_FMAC(5)   \
+      FA_DPP_FMAC(6) FA_DPP_FMAC(7) FA_DPP_FMAC(8) FA_DPP_FMAC(9) FA_DPP_FMAC(10) FA_DPP_FMAC(11)          \
+      FA_DPP_FMAC(12) FA_DPP_FMAC(13) FA_DPP_FMAC(14) FA_DPP_FMAC(15)                                     \
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),   \
+        "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),         \
+        "+v"(v[15])                                                                                    \
+      : "v"(g))
+    if constexpr (X == 1) {
+#define QP "quad_perm:[1,0,3,2]"
+      FA_DPP_BLOCK;
+#undef QP
+    } else {
+#define QP "quad_perm:[2,3,0,1]"
+      FA_DPP_BLOCK;
+#undef QP
+    }
+#undef FA_DPP_BLOCK
+#undef FA_DPP_FMAC
+  }
+}
+
+// sign (+1 / -1) of a lane's values after hadamard16_signed
+template <int SEG>
+__device__ __forceinline__ float hadamard_lane_sign(int sl) {
+  return (__builtin_popcount(sl & (SEG > 2 ? 3 : SEG - 1)) & 1) ? -1.f : 1.f;
+}
+
 template <int X, int SEG>
 __device__ __forceinline__ float cross_sum(float a) {
   if constexpr (X < SEG) return a + lane_xor<X>(a);
@@ -65,12 +108,14 @@ __device__ __forceinline__ float cross_sum(float a) {
 }
 
 // in-place Walsh-Hadamard (Sylvester order) over the d = 16 SEG values of a segment;
-// v[CE j + e] is channel 16 sl + CE j + e
-template <int CE, int SEG>
+// v[CE j + e] is channel 16 sl + CE j + e.  H0 = 2 when the caller has done the stage over
+// channel bit 0 itself.  SIGNED: the quad-lane stages leave the lane's values multiplied by
+// hadamard_lane_sign<SEG>(sl).
+template <int CE, int SEG, int H0 = 1, bool SIGNED = false>
 __device__ __forceinline__ void hadamard16(float (&v)[16], int sl) {
   constexpr int NCH = Lay<CE>::NCH;
 #pragma unroll
-  for (int h = 1; h < CE; h <<= 1)          // channel bits of e
+  for (int h = H0; h < CE; h <<= 1)         // channel bits of e
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if ((i & h) == 0) {
@@ -78,8 +123,13 @@ __device__ __forceinline__ void hadamard16(float (&v)[16], int sl) {
         v[i] = a + b;
         v[i + h] = a - b;
       }
-  cross_stage<1, SEG>(v, sl);                // channel bits of sl
-  cross_stage<2, SEG>(v, sl);
+  if constexpr (SIGNED) {                    // channel bits of sl
+    cross_stage_signed<1, SEG>(v, sl);
+    cross_stage_signed<2, SEG>(v, sl);
+  } else {
+    cross_stage<1, SEG>(v, sl);
+    cross_stage<2, SEG>(v, sl);
+  }
   cross_stage<4, SEG>(v, sl);
   cross_stage<8, SEG>(v, sl);
 #pragma unroll
@@ -138,24 +188,23 @@ __device__ __forceinline__ unsigned tq_code(float u, const float (&tp)[7]) {
   return (unsigned)((cnt ^ m) + H);
 }
 
-// The same 4-bit count by table: the float bits of x (clamped to [2^-7, 2)) name one of 64
-// buckets, eight per binade (bits 20..25: the exponent's low three bits and the top three
-// mantissa bits).  Entry b holds the positive threshold inside bucket b (its bits, or all ones if
-// none) and the number of positive thresholds below the bucket, so the count at x is
-// base + (x >= thr), with x compared unclamped.  Valid when no bucket holds two thresholds and the
-// smallest is at least 2^-7 (checked on the host; the search above serves other codebooks).
+// The same 4-bit code by table: the sign of u and the float bits of |u| (clamped to [2^-7, 2))
+// name one of 128 buckets, eight per binade and sign (index bit 6: the sign; bits 0..5: the
+// exponent's low three bits and the top three mantissa bits).  Entry b holds the threshold inside
+// bucket b (its float bits, or +inf if none) and the number of thresholds below the whole bucket,
+// so the code, the number of thresholds <= u, is base + (u >= thr) with u compared unclamped.
+// Valid when every nonzero threshold has 2^-7 <= |t| < 2 and no bucket holds two (checked on the
+// host; the search above serves other codebooks).  u must not be -0.
 constexpr unsigned kTabLo = 0x3C000000u;   // 2^-7
 constexpr unsigned kTabHi = 0x3FFFFFFFu;   // the float below 2
-__host__ __device__ inline unsigned tab_bucket_lo(unsigned b) { return ((120u + (b >> 3)) << 23) | ((b & 7u) << 20); }
+__host__ __device__ inline unsigned tab_bucket_lo(unsigned b) { return ((120u + ((b & 63u) >> 3)) << 23) | ((b & 7u) << 20); }
 
 __device__ __forceinline__ unsigned tq_code4_tab(float u, const u32x2* tab) {
   const unsigned ub = __float_as_uint(u);
-  const unsigned m = (unsigned)((int)ub >> 31);
-  const unsigned xb = (ub & 0x7fffffffu) + m;   // |u|, or the float just below it when u < 0
-  const unsigned cb = min(max(xb, kTabLo), kTabHi);
-  const u32x2 e = tab[(cb >> 20) & 63u];
-  const unsigned cnt = e[1] + (xb >= e[0] ? 1u : 0u);
-  return (cnt ^ m) + 8u;
+  // |u| clamped as a float (one med3 with the absolute value as an input modifier)
+  const unsigned cb = __float_as_uint(__builtin_amdgcn_fmed3f(fabsf(u), __uint_as_float(kTabLo), __uint_as_float(kTabHi)));
+  const u32x2 e = tab[((ub >> 25) & 64u) | ((cb >> 20) & 63u)];
+  return e[1] + (u >= __uint_as_float(e[0]) ? 1u : 0u);
 }
 
 // Row groups (RPW rows, one per segment) a wave takes in turn, the channel factors set up once
@@ -186,19 +235,9 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
   float tp[7];
 #pragma unroll
   for (int k = 0; k < 7; ++k) tp[k] = a.thr[(1 << (BITS - 1)) + (k < (1 << (BITS - 1)) - 1 ? k : 0)];
-  __shared__ u32x2 tab[TABLE ? 64 : 1];
+  __shared__ u32x2 tab[TABLE ? 128 : 1];
   if constexpr (TABLE) {
-    if (threadIdx.x < 64) {
-      const unsigned lo = tab_bucket_lo(threadIdx.x), hi = lo + (1u << 20);
-      unsigned base = 0, thr = 0xffffffffu;
-#pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        const unsigned tb = __float_as_uint(tp[k]);
-        base += tb < lo ? 1u : 0u;
-        thr = (tb >= lo && tb < hi) ? tb : thr;
-      }
-      tab[threadIdx.x] = u32x2{thr, base};
-    }
+    if (threadIdx.x < 128) tab[threadIdx.x] = u32x2{a.tab[threadIdx.x][0], a.tab[threadIdx.x][1]};
     __syncthreads();
   }
   const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqEncIter;
@@ -227,26 +266,44 @@ __global__ __launch_bounds__(256) void tq_encode_kernel(TqArgs a) {
     }
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ss = __builtin_fmaf(v[i], v[i], ss);
-      v[i] *= f[i];
+    for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    // the random signs (f = +-1, exact products) fused into the butterflies over channel bit 0:
+    // fma(f1, x1, f0 x0) rounds exactly like f0 x0 + f1 x1
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float t = v[i] * f[i], b = v[i + 1];
+      v[i] = __builtin_fmaf(f[i + 1], b, t);
+      v[i + 1] = __builtin_fmaf(-f[i + 1], b, t);
     }
     const float n = __fsqrt_rn(segment_sum<SEG>(ss));
-    hadamard16<CE, SEG>(v, sl);
+    hadamard16<CE, SEG, 2, true>(v, sl);
     float yy = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) yy = __builtin_fmaf(v[i], v[i], yy);
     const float ny = __fsqrt_rn(segment_sum<SEG>(yy));
-    const float inv = ny > 0.f ? __fdiv_rn(1.0f, ny) : 0.f;
+    // 1 / ||y||, carrying the lane's Hadamard sign (exact: a sign flip of the rounded quotient)
+    const float inv = (ny > 0.f ? __fdiv_rn(1.0f, ny) : 0.f) * hadamard_lane_sign<SEG>(sl);
     if (row < a.n) {
-      // the lane's 16 codes, channel 16 sl + i at bit BITS i of a little-endian word of 16 BITS bits
-      uint64_t packed = 0;
+      // the lane's 16 codes, channel 16 sl + i at bit BITS i of a little-endian word of 16 BITS bits,
+      // assembled as two 32-bit halves (codes 0..7 and 8..15 at 4 bits; at 2 and 3 bits the high half
+      // holds what passes bit 31)
+      unsigned w0 = 0, w1 = 0;
       // fma with +0 rounds like the product and turns a -0 product into +0
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        packed |= (uint64_t)(TABLE ? tq_code4_tab(__builtin_fmaf(v[i], inv, 0.0f), tab)
-                                   : tq_code<BITS>(__builtin_fmaf(v[i], inv, 0.0f), tp))
-                  << (BITS * i);
+      for (int i = 0; i < 16; ++i) {
+        const unsigned code = TABLE ? tq_code4_tab(__builtin_fmaf(v[i], inv, 0.0f), tab)
+                                    : tq_code<BITS>(__builtin_fmaf(v[i], inv, 0.0f), tp);
+        const int b = BITS * i;
+        if (b + BITS <= 32) {
+          w0 |= code << b;
+        } else if (b >= 32) {
+          w1 |= code << (b - 32);
+        } else {   // a 3-bit code across bit 32
+          w0 |= code << b;
+          w1 |= code >> (32 - b);
+        }
+      }
+      const uint64_t packed = (uint64_t)w0 | ((uint64_t)w1 << 32);
       uint8_t* dst = a.codes + row * (D * BITS / 8) + sl * (2 * BITS);
       if constexpr (BITS == 4) {
         *reinterpret_cast<u32x2*>(dst) = u32x2{(unsigned)packed, (unsigned)(packed >> 32)};
@@ -294,8 +351,8 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
       pk[it] = *reinterpret_cast<const unsigned*>(src);
     }
   }
-  float f[16];
-  channel_factors<CE, SEG>(f, a.signs, sl, a.inv_sqrt_d);
+  float f[16];   // sign * 1/sqrt(d), times the lane's Hadamard sign
+  channel_factors<CE, SEG>(f, a.signs, sl, a.inv_sqrt_d * hadamard_lane_sign<SEG>(sl));
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < kTqDecIter; ++it) {
@@ -306,7 +363,7 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       v[i] = mul_rn(nn[it], cb[(unsigned)(pk[it] >> (BITS * i)) & ((1u << BITS) - 1)]);
-    hadamard16<CE, SEG>(v, sl);
+    hadamard16<CE, SEG, 1, true>(v, sl);
     if (row < a.n) {
       float y[16];
 #pragma unroll
@@ -328,27 +385,47 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   }
 }
 
-// the table decision applies (4 bits; positive thresholds a.thr[8 ..] in distinct buckets, the
-// smallest at least 2^-7, the largest below 2)
-inline bool tq_table_ok(const TqArgs& a) {
-  unsigned prev = 0;
-  for (int k = 0; k < 7; ++k) {
+// The 4-bit decision table (host): true and a.tab filled when every nonzero threshold has
+// 2^-7 <= |t| < 2 and no (sign, bucket) holds two.
+inline bool tq_table_build(TqArgs& a) {
+  int seen[128] = {0};
+  for (int k = 0; k < 15; ++k) {
     unsigned tb;
-    std::memcpy(&tb, &a.thr[8 + k], 4);
-    if (tb < kTabLo || tb > kTabHi) return false;
-    if (k > 0 && (tb >> 20) == (prev >> 20)) return false;
-    prev = tb;
+    std::memcpy(&tb, &a.thr[k], 4);
+    const unsigned ab = tb & 0x7fffffffu;
+    if (ab == 0u) continue;
+    if (ab < kTabLo || ab > kTabHi) return false;
+    if (seen[((tb >> 25) & 64u) | ((ab >> 20) & 63u)]++) return false;
+  }
+  for (unsigned t = 0; t < 128; ++t) {
+    const bool neg = t >= 64u;
+    const unsigned lo = tab_bucket_lo(t), hi = lo + (1u << 20);
+    unsigned base = 0, tbits = 0x7f800000u;   // +inf: no threshold inside the bucket
+    for (int k = 0; k < 15; ++k) {
+      const float x = a.thr[k];
+      unsigned xb;
+      std::memcpy(&xb, &x, 4);
+      const unsigned ab = xb & 0x7fffffffu;
+      if (ab != 0u && (x < 0.f) == neg && ab >= lo && ab < hi) {
+        tbits = xb;                            // compared against u
+      } else if (neg ? (x < 0.f && ab >= hi) : (x <= 0.f || ab < lo)) {
+        ++base;                                // at or below every u of the bucket
+      }
+    }
+    a.tab[t][0] = tbits;
+    a.tab[t][1] = base;
   }
   return true;
 }
 
 template <int D, int BITS>
-hipError_t launch_encode_d(const TqArgs& a, bool bf16, hipStream_t st, const char** name) {
+hipError_t launch_encode_d(const TqArgs& a_in, bool bf16, hipStream_t st, const char** name) {
+  TqArgs a = a_in;
   const int64_t rows_per_block = 4 * (64 / (D / 16)) * kTqEncIter;
   const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(256);
-  if (BITS == 4 && tq_table_ok(a)) {
+  if (BITS == 4 && tq_table_build(a)) {
     if (bf16) hipLaunchKernelGGL((tq_encode_kernel<D, true, BITS, BITS == 4>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((tq_encode_kernel<D, false, BITS, BITS == 4>), grid, block, 0, st, a);
     *name = "tq_encode";
