@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--legs", default="c5,c5w,c3,c4,c4g8,comp,append,merge,tq,tqattn")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the rocm-smi clock sampling (for runs under a profiler, whose preload would "
+                         "follow the rocm-smi child process)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -215,7 +218,7 @@ def main():
                          "flop_per_launch": flops, "tflops": flops / avg / 1e9,
                          "frac_of_peak": flops / avg / 1e9 / PEAK_BF16_TFLOPS}
             log(f"[bench] {name}: {avg:.3f} ms  {res[name]['tflops']:.1f} TFLOP/s")
-            if name == "c5":
+            if name == "c5" and not args.no_clock:
                 mhz = shader_clock_under_load(torch, fn)
                 res[name]["clock_mhz"] = mhz
                 if mhz:
