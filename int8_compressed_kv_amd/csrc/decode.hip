@@ -299,8 +299,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
 
   auto compute = [&](int idx, bool valid, const Tile& T) {
     const int k0 = a.key_lo + (ts + wave_u + kWaves * idx) * KT;
-    // V rows and the scales into the wave's LDS slot (row r, chunk c at chunk c ^ swz(r));
-    // the previous tile's reads of the slot were consumed before this point.
+    // V rows and the scales into the wave's LDS slot (row r, chunk c at chunk c ^ swz(r)), after
+    // the previous tile's reads of it and before this tile's
+    wave_lds_order();
 #pragma unroll
     for (int u = 0; u < VCH; ++u) {
       const int Fc = 64 * u + lane;
@@ -309,6 +310,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     }
 #pragma unroll
     for (int e = 0; e < NSC; ++e) reinterpret_cast<float*>(slot + KT * D)[64 * e + lane] = T.sc[e];
+    wave_lds_order();
     const unsigned char* vb_ = slot;
     const float* sk = reinterpret_cast<const float*>(slot + KT * D);
     const float* sv = sk + KT;

@@ -174,4 +174,10 @@ __device__ __forceinline__ void apply_score_ops(float (&x)[N], const EpiArgs& e,
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
+// Lanes of one wave exchanging data through a wave-private LDS slot: the hardware performs a
+// wave's LDS accesses in order, so the compiler only has to keep them in program order, which it
+// would not otherwise do where it can prove that one lane's own accesses do not overlap (no
+// memory access moves across this).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
 }  // namespace fa

@@ -11,50 +11,83 @@
 // forward.  The Mul/Add epilogue runs on the merged row, before the cast.
 //
 // HBM-bound: a segment of D/4 lanes owns a row, each lane reading 16 contiguous bytes of every
-// part (nontemporal: each byte is read once), four parts' loads in flight at a time.
+// part (nontemporal loads and stores: each byte is read or written once).  Up to eight parts are
+// handled per group with every load of the group -- their LSE values and their output rows --
+// issued before the first use, so a wave waits for memory once per group rather than once per
+// part; with more than eight parts a first pass finds M over the LSE values, eight loads in
+// flight at a time.
 #include "device_common.hpp"
 
 namespace fa {
 namespace {
 
+constexpr int kPartGroup = 8;   // parts whose loads are in flight together
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int SEG = D / 4;     // lanes per row
   constexpr int RPW = 64 / SEG;  // rows per wave (D <= 256, so SEG <= 64)
+  constexpr int PG = kPartGroup;
   static_assert(D % 32 == 0 && SEG <= 64, "head_dim must be a multiple of 32, at most 256");
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
   const int64_t row = (((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / SEG;
   if (row >= a.rows) return;     // rows are independent: no lane exchange below
   const float* lse = a.lse_parts + row;
+  const float* src = a.o_parts + row * D + 4 * sl;
+  const int n = a.n_parts;
+
+  float lp[PG];
+  f32x4 x[PG];
+  // loads of parts p .. p + 7 (those below n; a missing part reads as LSE -inf, weight 0)
+  auto load_group = [&](int p) {
+#pragma unroll
+    for (int u = 0; u < PG; ++u) {
+      if (p + u < n) {
+        lp[u] = lse[(int64_t)(p + u) * a.rows];
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (int64_t)(p + u) * a.rows * D));
+      } else {
+        lp[u] = neg_inf();
+        x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
   float m = neg_inf();
-  for (int p = 0; p < a.n_parts; ++p) m = fmaxf(m, lse[(int64_t)p * a.rows]);
+  if (n <= PG) {
+    load_group(0);
+#pragma unroll
+    for (int u = 0; u < PG; ++u) m = fmaxf(m, lp[u]);
+  } else {
+    for (int p = 0; p < n; p += PG) {
+      float lq[PG];
+#pragma unroll
+      for (int u = 0; u < PG; ++u) lq[u] = p + u < n ? lse[(int64_t)(p + u) * a.rows] : neg_inf();
+#pragma unroll
+      for (int u = 0; u < PG; ++u) m = fmaxf(m, lq[u]);
+    }
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
   const float mm = m == neg_inf() ? 0.f : m;   // every weight is then 0 for an uncovered row
-  const float* src = a.o_parts + row * D + 4 * sl;
   // a part of weight 0 adds nothing even if its row holds garbage (select, not multiply)
-  auto add_part = [&](float lp, const f32x4& x) {
-    const float w = __builtin_amdgcn_exp2f((lp - mm) * 1.4426950408889634f);
-    l += w;
+  auto add_group = [&]() {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = w > 0.f ? __builtin_fmaf(w, x[e], acc[e]) : acc[e];
-  };
-  int p = 0;
-  for (; p + 4 <= a.n_parts; p += 4) {   // four parts' loads in flight together
-    float lp[4];
-    f32x4 x[4];
+    for (int u = 0; u < PG; ++u) {
+      const float w = __builtin_amdgcn_exp2f((lp[u] - mm) * 1.4426950408889634f);
+      l += w;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lp[u] = lse[(int64_t)(p + u) * a.rows];
-      x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (int64_t)(p + u) * a.rows * D));
+      for (int e = 0; e < 4; ++e) acc[e] = w > 0.f ? __builtin_fmaf(w, x[u][e], acc[e]) : acc[e];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) add_part(lp[u], x[u]);
+  };
+  if (n <= PG) {
+    add_group();
+  } else {
+    for (int p = 0; p < n; p += PG) {
+      load_group(p);
+      add_group();
+    }
   }
-  for (; p < a.n_parts; ++p)
-    add_part(lse[(int64_t)p * a.rows],
-             __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (int64_t)p * a.rows * D)));
   const float inv = l > 0.f ? __fdiv_rn(1.0f, l) : 0.f;
   float y[4];
 #pragma unroll
@@ -62,10 +95,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   apply_epilogue_all(y, a.epi, [&](int e) { return 4 * sl + e; });
   if (a.out_bf16) {
     const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + 4 * sl) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<unsigned short*>(a.out) + row * D + 4 * sl));
   } else {
     const f32x4 w = {y[0], y[1], y[2], y[3]};
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + 4 * sl) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + 4 * sl));
   }
   if (a.lse && sl == 0) a.lse[row] = l > 0.f ? m + logf(l) : neg_inf();
 }

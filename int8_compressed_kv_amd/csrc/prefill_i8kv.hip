@@ -152,15 +152,107 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   const int n_tiles = hi > lo ? (hi + BN - 1) / BN - t_lo : 0;
   const int64_t kv_base = (int64_t)kvh * a.s_k;
 
+  const int8_t* kp8 = static_cast<const int8_t*>(a.k) + kv_base * D;
+  const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
+  const int last_key = a.s_k - 1;
+
+  // Staging order of the 16-code chunks of a tile (head_dim 64 / 128): position pos holds chunk
+  // pos % NCR of row staged_row(pos).  Each block of 8 rows is staged in the row order
+  // 0, 4, 1, 5, 2, 6, 3, 7, so the 16 threads of a quarter-wave, which convert 16 consecutive
+  // positions, cover rows whose swizzles differ in bit 0 (row bit 2): their 16-byte operand writes
+  // then fall into distinct bank groups, while their reads of the staging stage stay contiguous.
+  constexpr int NCR = D / 16;   // 16-code chunks per row
+  auto staged_row = [&](int pos) __attribute__((always_inline)) {
+    const int blk = pos / (8 * NCR), slot = (pos % (8 * NCR)) / NCR;
+    return 8 * blk + (slot >> 1) + 4 * (slot & 1);
+  };
+
+  // ---- direct global -> LDS staging (head_dim 64 / 128)
+  // Per tile: wave w copies K/V segments SPW w .. SPW w + SPW - 1 (segment gs < SEGS is K
+  // segment gs, else V segment gs - SEGS; lane l of a segment brings the 16 codes of staging
+  // position 64 seg + l), wave 0 the 64 k scales and wave 1 the 64 v scales.
+  // Tiles 0 .. 2 are copied in the prologue; tile t + 3's copies are issued in iteration t,
+  // after the barrier that ended the conversion
+  // of tile t - 1 (the last reader of that staging stage, in iteration t - 2); each wave waits
+  // for its own copies of tile t + 3 at the end of iteration t + 1, before the barrier that
+  // precedes their conversion in iteration t + 2.
+  const unsigned q8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int8_t*)&lds_q8[0][0];
+  const unsigned s8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)&lds_s8[0][0];
+  int crow[SPW], ccol[SPW];
+  unsigned voff[SPW], seg_lds[SPW];
+  const int8_t* cbase[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int gs = SPW * wave + j;
+    const int mat = gs / SEGS, seg = gs % SEGS;
+    const int pos = 64 * seg + lane;            // 16-byte staging position within the matrix
+    crow[j] = staged_row(pos);
+    ccol[j] = 16 * (pos % NCR);
+    voff[j] = (unsigned)(crow[j] * D + ccol[j]);
+    cbase[j] = mat ? vp8 : kp8;
+    seg_lds[j] = __builtin_amdgcn_readfirstlane(q8_0 + (unsigned)(mat * BN * D + 1024 * seg));
+  }
+  const float* sc_src = wave == 0 ? a.k_scale : a.v_scale;
+  const unsigned sc_lds = s8_0 + (wave == 0 ? 0u : 4u * BN);
+  auto copy_tile = [&](int t) __attribute__((always_inline)) {
+    const int k0 = (t_lo + t) * BN;
+    const unsigned st_off = (unsigned)(Q8 * (t % NS8));
+    if (k0 + BN <= a.s_k) {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) copy16_to_lds(cbase[j] + (int64_t)k0 * D, voff[j], seg_lds[j] + st_off);
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
+        copy16_to_lds(cbase[j] + row * D + ccol[j], seg_lds[j] + st_off);
+      }
+    }
+    if (wave < 2)
+      copy4_to_lds(sc_src + kv_base + min(k0 + lane, last_key), sc_lds + (unsigned)(4 * 2 * BN * (t % NS8)));
+  };
+  // the copies of the latest tile may stay in flight; those of the one before must have landed
+  auto wait_all_but_latest = [&]() __attribute__((always_inline)) {
+    if (wave < 2) wait_vmcnt<SPW + 1>();
+    else wait_vmcnt<SPW>();
+  };
+
+  // ---- prologue: the first three tiles' copies, the Q rows and the block's scales are all issued
+  // before the first wait, so a block starts after one memory latency rather than one per step
+  if constexpr (DMA) {
+    if (n_tiles > 0) copy_tile(0);
+    if (n_tiles > 1) copy_tile(1);
+    if (n_tiles > 2) copy_tile(2);
+  }
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + c;
+  const unsigned short* qp = static_cast<const unsigned short*>(a.q) + (int64_t)head * a.s_q * D;
+  u32x4 qraw[NKS];
+  {
+    const int64_t qrow = min(qi, a.s_q - 1);   // rows past the end load the last row, then read as 0
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + qrow * D + 16 * ks + 8 * h);
+  }
+
   // ---- int8: power-of-two normalisers of the block's scales.  K~ = fp16(k) * fp16(k_s 2^-Ek) and
   // V~ = fp16(v) * fp16(v_s 2^-Ev), with 2^-Ek, 2^-Ev putting the largest scale over the keys of
   // the block's tiles in [128, 256), so that every |K~|, |V~| <= 127 * 256 stays inside fp16
-  // (also on masked keys, whose P = 0 must not meet an infinite V~)
+  // (also on masked keys, whose P = 0 must not meet an infinite V~).  Eight scales of each matrix
+  // per thread are loaded together (indices clamped to the range: repeats leave the max as is).
   float mk = 0.f, mv = 0.f;
   const int key_end = min(a.s_k, (t_lo + n_tiles) * BN);
-  for (int j = t_lo * BN + tid; j < key_end; j += 64 * NW) {
-    mk = fmaxf(mk, a.k_scale[kv_base + j]);
-    mv = fmaxf(mv, a.v_scale[kv_base + j]);
+  for (int j0 = t_lo * BN; j0 < key_end; j0 += 8 * 64 * NW) {
+    float kk[8], vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + tid + 64 * NW * u, key_end - 1);
+      kk[u] = a.k_scale[kv_base + j];
+      vv[u] = a.v_scale[kv_base + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mk = fmaxf(mk, kk[u]);
+      mv = fmaxf(mv, vv[u]);
+    }
   }
 #pragma unroll
   for (int o2 = 32; o2 >= 1; o2 >>= 1) {
@@ -171,6 +263,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     lds_red[0][wave] = mk;
     lds_red[1][wave] = mv;
   }
+  if constexpr (DMA) wait_vmcnt<0>();   // the first tiles' copies, published by the barrier
   __syncthreads();
   mk = 0.f;
   mv = 0.f;
@@ -192,15 +285,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   // with 2^-Eq putting the row's largest |q| in [2^14, 2^15) (bf16 -> fp16 is then exact down to
   // 2^-28 of that largest value).  S~ = Q~ K~^T is S / (2^-Eq 2^-Ek): the row's exp2-domain factor
   // c2row absorbs both powers of two.
-  const int qw0 = q0 + 32 * wave;
-  const int qi = qw0 + c;
-  const unsigned short* qp = static_cast<const unsigned short*>(a.q) + (int64_t)head * a.s_q * D;
-  u32x4 qraw[NKS];
   float qmax = 0.f;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    qraw[ks] = u32x4{0u, 0u, 0u, 0u};
-    if (qi < a.s_q) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + (int64_t)qi * D + 16 * ks + 8 * h);
+    if (qi >= a.s_q) qraw[ks] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2)
       qmax = fmaxf(qmax, fmaxf(fabsf(__uint_as_float(qraw[ks][e2] << 16)), fabsf(__uint_as_float(qraw[ks][e2] & 0xffff0000u))));
@@ -221,10 +309,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   }
   // S = S~ 2^(eq - 15) 2^(ek - 8)
   const int es = (eq - 15) + (ek - 8);
-
-  const int8_t* kp8 = static_cast<const int8_t*>(a.k) + kv_base * D;
-  const int8_t* vp8 = static_cast<const int8_t*>(a.v) + kv_base * D;
-  const int last_key = a.s_k - 1;
 
   // ---- per-wave state
   f32x16 O[NDB];
@@ -400,64 +484,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     return f16x2{hv, hv};
   };
 
-  // Staging order of the 16-code chunks of a tile (head_dim 64 / 128): position pos holds chunk
-  // pos % NCR of row staged_row(pos).  Each block of 8 rows is staged in the row order
-  // 0, 4, 1, 5, 2, 6, 3, 7, so the 16 threads of a quarter-wave, which convert 16 consecutive
-  // positions, cover rows whose swizzles differ in bit 0 (row bit 2): their 16-byte operand writes
-  // then fall into distinct bank groups, while their reads of the staging stage stay contiguous.
-  constexpr int NCR = D / 16;   // 16-code chunks per row
-  auto staged_row = [&](int pos) __attribute__((always_inline)) {
-    const int blk = pos / (8 * NCR), slot = (pos % (8 * NCR)) / NCR;
-    return 8 * blk + (slot >> 1) + 4 * (slot & 1);
-  };
-
   if constexpr (DMA) {
-    // Per tile: wave w copies K/V segments SPW w .. SPW w + SPW - 1 (segment gs < SEGS is K
-    // segment gs, else V segment gs - SEGS; lane l of a segment brings the 16 codes of staging
-    // position 64 seg + l), wave 0 the 64 k scales and wave 1 the 64 v scales.
-    // Tile t + 3's copies are issued in iteration t, after the barrier that ended the conversion
-    // of tile t - 1 (the last reader of that staging stage, in iteration t - 2); each wave waits
-    // for its own copies of tile t + 3 at the end of iteration t + 1, before the barrier that
-    // precedes their conversion in iteration t + 2.
-    const unsigned q8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int8_t*)&lds_q8[0][0];
-    const unsigned s8_0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)&lds_s8[0][0];
-    int crow[SPW], ccol[SPW];
-    unsigned voff[SPW], seg_lds[SPW];
-    const int8_t* cbase[SPW];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int gs = SPW * wave + j;
-      const int mat = gs / SEGS, seg = gs % SEGS;
-      const int pos = 64 * seg + lane;            // 16-byte staging position within the matrix
-      crow[j] = staged_row(pos);
-      ccol[j] = 16 * (pos % NCR);
-      voff[j] = (unsigned)(crow[j] * D + ccol[j]);
-      cbase[j] = mat ? vp8 : kp8;
-      seg_lds[j] = __builtin_amdgcn_readfirstlane(q8_0 + (unsigned)(mat * BN * D + 1024 * seg));
-    }
-    const float* sc_src = wave == 0 ? a.k_scale : a.v_scale;
-    const unsigned sc_lds = s8_0 + (wave == 0 ? 0u : 4u * BN);
-    auto copy_tile = [&](int t) __attribute__((always_inline)) {
-      const int k0 = (t_lo + t) * BN;
-      const unsigned st_off = (unsigned)(Q8 * (t % NS8));
-      if (k0 + BN <= a.s_k) {
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) copy16_to_lds(cbase[j] + (int64_t)k0 * D, voff[j], seg_lds[j] + st_off);
-      } else {
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
-          copy16_to_lds(cbase[j] + row * D + ccol[j], seg_lds[j] + st_off);
-        }
-      }
-      if (wave < 2)
-        copy4_to_lds(sc_src + kv_base + min(k0 + lane, last_key), sc_lds + (unsigned)(4 * 2 * BN * (t % NS8)));
-    };
-    // the copies of the latest tile may stay in flight; those of the one before must have landed
-    auto wait_all_but_latest = [&]() __attribute__((always_inline)) {
-      if (wave < 2) wait_vmcnt<SPW + 1>();
-      else wait_vmcnt<SPW>();
-    };
     // staging stage s8 -> operand stage st: thread tid converts chunk tid + 64 NW u of the 2 BN D / 16
     // chunks (K chunks first), scaling each row by its scale times the block normaliser
     auto convert = [&](auto s8, auto stage) __attribute__((always_inline)) {
@@ -491,18 +518,9 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
       }
       __syncthreads();
     };
+    // tiles 0 .. 2 landed before the prologue's barrier
     if (n_tiles > 0) {
-      copy_tile(0);
-      wait_vmcnt<0>();
-      __syncthreads();
       convert(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-      if (n_tiles > 1) copy_tile(1);
-      if (n_tiles > 2) {
-        copy_tile(2);
-        wait_all_but_latest();
-      } else {
-        wait_vmcnt<0>();
-      }
       __syncthreads();
     }
     using I0 = std::integral_constant<int, 0>;

@@ -213,7 +213,8 @@ __device__ __forceinline__ unsigned tq_code4_tab(float u, const u32x2* tab) {
 constexpr int kTqEncIter = 1;
 constexpr int kTqDecIter = 4;
 
-// The NCH 16-byte chunks of row r a lane holds (its 16 NCH contiguous bytes).
+// The NCH 16-byte chunks of row r a lane holds (its 16 NCH contiguous bytes).  (Loading the row
+// group as whole 1-KiB runs and handing each lane its chunks through LDS measured the same.)
 template <int ROW_BYTES, int SEG, int NCH>
 __device__ __forceinline__ void load_chunks(u32x4 (&w)[NCH], const void* x, int64_t r, int sl) {
   const char* p = static_cast<const char*>(x) + r * ROW_BYTES + 16 * NCH * sl;
@@ -327,11 +328,14 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
   constexpr int CE = 4;                       // fp32 values per chunk of the layout
   constexpr int SEG = D / 16;
   constexpr int RPW = 64 / SEG;
+  constexpr int NST = BF16_OUT ? 2 : 4;       // 16-byte output chunks per lane and row group
   __shared__ float cb[16];
+  __shared__ u32x4 slot[4][64 * NST];         // per wave: one row group's output
   if (threadIdx.x < 16) cb[threadIdx.x] = a.cb[threadIdx.x];
   const int lane = threadIdx.x & 63;
   const int sl = lane % SEG;
-  const int64_t g0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * kTqDecIter;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + wv) * kTqDecIter;
   // all row groups' codes (the lane's contiguous 16) and norms are loaded up front (rows past the
   // end repeat the last row)
   uint64_t pk[kTqDecIter];   // the lane's 16 codes, channel 16 sl + i at bit BITS i
@@ -357,30 +361,42 @@ __global__ __launch_bounds__(256) void tq_decode_kernel(TqArgs a) {
 #pragma unroll
   for (int it = 0; it < kTqDecIter; ++it) {
     if ((g0 + it) * RPW >= a.n) break;
-    const int64_t row = (g0 + it) * RPW + lane / SEG;
     float v[16];
     // rounded on its own: an fma with the first butterfly's add would round differently
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       v[i] = mul_rn(nn[it], cb[(unsigned)(pk[it] >> (BITS * i)) & ((1u << BITS) - 1)]);
     hadamard16<CE, SEG, 1, true>(v, sl);
-    if (row < a.n) {
-      float y[16];
+    float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = v[i] * f[i];
-      if constexpr (BF16_OUT) {
-        unsigned short* dst = static_cast<unsigned short*>(a.out) + row * D + 16 * sl;
+    for (int i = 0; i < 16; ++i) y[i] = v[i] * f[i];
+    // The group's RPW rows are one contiguous run of NST 16-byte chunks per lane (2 KiB of bf16,
+    // 4 KiB of fp32).  A lane's own chunks sit NST apart, so storing them directly would make
+    // every store instruction write every NST-th chunk of the run; they go through the wave's LDS
+    // slot instead, and store k of lane l writes chunk 64 k + l: each store covers 1 KiB whole.
+    u32x4 w[NST];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const u32x4 w = {pack_bf16x2(y[8 * h2], y[8 * h2 + 1]), pack_bf16x2(y[8 * h2 + 2], y[8 * h2 + 3]),
-                           pack_bf16x2(y[8 * h2 + 4], y[8 * h2 + 5]), pack_bf16x2(y[8 * h2 + 6], y[8 * h2 + 7])};
-          *reinterpret_cast<u32x4*>(dst + 8 * h2) = w;
-        }
-      } else {
-        float* dst = static_cast<float*>(a.out) + row * D + 16 * sl;
+    for (int j = 0; j < NST; ++j) {
+      if constexpr (BF16_OUT)
+        w[j] = u32x4{pack_bf16x2(y[8 * j], y[8 * j + 1]), pack_bf16x2(y[8 * j + 2], y[8 * j + 3]),
+                     pack_bf16x2(y[8 * j + 4], y[8 * j + 5]), pack_bf16x2(y[8 * j + 6], y[8 * j + 7])};
+      else
+        w[j] = u32x4{__float_as_uint(y[4 * j]), __float_as_uint(y[4 * j + 1]), __float_as_uint(y[4 * j + 2]),
+                     __float_as_uint(y[4 * j + 3])};
+    }
+    wave_lds_order();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(dst + 4 * j) = f32x4{y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]};
-      }
+    for (int j = 0; j < NST; ++j) slot[wv][NST * lane + j] = w[j];
+    wave_lds_order();
+#pragma unroll
+    for (int k = 0; k < NST; ++k) w[k] = slot[wv][64 * k + lane];
+    wave_lds_order();
+    const int64_t row0 = (g0 + it) * RPW;
+    char* dst = static_cast<char*>(a.out) + row0 * D * (BF16_OUT ? 2 : 4);
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int chunk = 64 * k + lane;
+      if (row0 + chunk / (NST * SEG) < a.n) *reinterpret_cast<u32x4*>(dst + 16 * chunk) = w[k];
     }
   }
 }

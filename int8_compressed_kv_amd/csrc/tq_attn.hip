@@ -296,6 +296,9 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
 
   auto compute = [&](int idx, bool valid, const Tile& T) {
     const int k0 = a.key_lo + (ts + wave_u + kTqWaves * idx) * KT;
+    // V codes and the norms into the wave's LDS slot, after the previous tile's reads of it and
+    // before this tile's
+    wave_lds_order();
 #pragma unroll
     for (int u = 0; u < VCH; ++u) {
       const int Fc = 64 * u + lane;
@@ -304,6 +307,7 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
     }
     reinterpret_cast<float*>(slot + KT * RV)[lane] = T.nrm[0];
     reinterpret_cast<float*>(slot + KT * RV)[64 + lane] = T.nrm[1];
+    wave_lds_order();
     const float* snk = reinterpret_cast<const float*>(slot + KT * RV);
     const float* snv = snk + KT;
     const bool tail = !valid || k0 + KT > a.s_k;

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 def test_merge_random_parts(d):
     import int8_compressed_kv_amd as fa
     torch = torch_gpu()
-    for n_parts, rows in [(1, 7), (2, 300), (5, 1000), (17, 65)]:
+    for n_parts, rows in [(1, 7), (2, 300), (5, 1000), (8, 129), (9, 64), (17, 65)]:
         say(f"merge d={d} parts={n_parts} rows={rows}")
         o = rng_normal(800 + d + n_parts, (n_parts, rows, d))[0]
         g = np.random.Generator(np.random.PCG64(n_parts * 100 + d))
