@@ -138,16 +138,28 @@ def shader_clock_under_load(torch, fn, seconds=2.0):
 
 
 class Timer:
-    """HIP events around each call on the current stream; returns per-call milliseconds."""
+    """HIP events around each call on the current stream; returns per-call milliseconds.
 
-    def __init__(self, torch):
+    `warm_s`: after the `warmup` calls, keep calling until that much wall time has passed, so a leg
+    is timed at the clock the GPU settles to under it (the first tens of milliseconds of a short
+    kernel run below it: about 830 us against 677 us per int8-cache prefill call on one box).  The
+    headline leg uses exactly the `--warmup` calls."""
+
+    def __init__(self, torch, warm_s=0.0):
         self.torch = torch
+        self.warm_s = warm_s
 
-    def run(self, fn, steps, warmup, flush=None):
+    def run(self, fn, steps, warmup, flush=None, settle=True):
         torch = self.torch
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        if settle and self.warm_s > 0:
+            t0 = time.time()
+            while time.time() - t0 < self.warm_s:
+                for _ in range(4):
+                    fn()
+                torch.cuda.synchronize()
         times = []
         for _ in range(steps):
             if flush is not None:
@@ -169,6 +181,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="c5,c5w,c3,c4,c4g8,comp,append,merge,tq,tqattn")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--settle", type=float, default=0.25,
+                    help="seconds of extra untimed calls before each leg other than the headline c5 (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget per baseline")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the rocm-smi clock sampling (for runs under a profiler, whose preload would "
@@ -187,7 +201,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     legs = set(args.legs.split(","))
-    timer = Timer(torch)
+    timer = Timer(torch, warm_s=args.settle)
     res = {}
     flush_buf = torch.zeros(512 * 1024 * 1024, dtype=torch.float32, device="cuda")   # 2 GiB > MALL
     flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
@@ -216,7 +230,7 @@ def main():
             flops = 4.0 * w.d * visible_pairs(w.s_q, w.s_k, True, window) * w.bh_q
             fn = lambda: fa.flash_attention(qd, kd, vd, causal=True, window=window, out=out)   # noqa: E731
             log(f"[bench] timing {ww.name}")
-            ms = timer.run(fn, args.steps, args.warmup)
+            ms = timer.run(fn, args.steps, args.warmup, settle=name != "c5")
             avg = float(np.mean(ms))
             res[name] = {"workload": ww.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
                          "flop_per_launch": flops, "tflops": flops / avg / 1e9,
