@@ -157,14 +157,21 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
   const int last_key = a.s_k - 1;
 
   // Staging order of the 16-code chunks of a tile (head_dim 64 / 128): position pos holds chunk
-  // pos % NCR of row staged_row(pos).  Each block of 8 rows is staged in the row order
-  // 0, 4, 1, 5, 2, 6, 3, 7, so the 16 threads of a quarter-wave, which convert 16 consecutive
-  // positions, cover rows whose swizzles differ in bit 0 (row bit 2): their 16-byte operand writes
-  // then fall into distinct bank groups, while their reads of the staging stage stay contiguous.
+  // staged_chunk(pos) of row staged_row(pos).  Within a block of 8 rows, consecutive positions run
+  // over 4 chunks of row g, the same 4 chunks of row g + 4, (at head_dim 128) the next 4 chunks
+  // of both rows, then the next g.  So any 8 threads converting consecutive positions cover two
+  // rows whose swizzles differ in bit 0 (row bit 2) and 4 chunks of each: the 8 16-byte operand
+  // writes of such a group land in 8 distinct chunk positions modulo 8, which keeps them in
+  // distinct banks whether the LDS serves 8 or 16 lanes of a 16-byte write at a time, while
+  // their reads of the staging stage stay contiguous.
   constexpr int NCR = D / 16;   // 16-code chunks per row
   auto staged_row = [&](int pos) __attribute__((always_inline)) {
-    const int blk = pos / (8 * NCR), slot = (pos % (8 * NCR)) / NCR;
-    return 8 * blk + (slot >> 1) + 4 * (slot & 1);
+    const int q = pos % (8 * NCR);
+    return 8 * (pos / (8 * NCR)) + q / (2 * NCR) + 4 * ((q >> 2) & 1);
+  };
+  auto staged_chunk = [&](int pos) __attribute__((always_inline)) {
+    const int q = pos % (8 * NCR);
+    return 4 * ((q >> 3) % (NCR / 4)) + (q & 3);
   };
 
   // ---- direct global -> LDS staging (head_dim 64 / 128)
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     const int mat = gs / SEGS, seg = gs % SEGS;
     const int pos = 64 * seg + lane;            // 16-byte staging position within the matrix
     crow[j] = staged_row(pos);
-    ccol[j] = 16 * (pos % NCR);
+    ccol[j] = 16 * staged_chunk(pos);
     voff[j] = (unsigned)(crow[j] * D + ccol[j]);
     cbase[j] = mat ? vp8 : kp8;
     seg_lds[j] = __builtin_amdgcn_readfirstlane(q8_0 + (unsigned)(mat * BN * D + 1024 * seg));
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
         const bool is_v = ci >= NCH8 / 2;
         const int cm = is_v ? ci - NCH8 / 2 : ci;
         const u32x4 w = *reinterpret_cast<const u32x4*>(&lds_q8[static_cast<int>(s8)][16 * ci]);
-        const int r = staged_row(cm), lc = 2 * (cm % NCR);
+        const int r = staged_row(cm), lc = 2 * staged_chunk(cm);
         const f16x2 sr = half2_of(lds_s8[static_cast<int>(s8)][(is_v ? BN : 0) + r] * (is_v ? vs_norm : ks_norm));
         const u32x2 x0 = scaled4(w[0], sr), x1 = scaled4(w[1], sr);
         const u32x2 x2 = scaled4(w[2], sr), x3 = scaled4(w[3], sr);
