@@ -516,7 +516,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
     auto iter = [&](int t, auto st, auto st1, auto s81) __attribute__((always_inline)) {
       if (t >= n_tiles) return;
       compute(t, st);
-      if (t + 1 < n_tiles) convert(s81, st1);
+      // unconditional, so that it shares a basic block with the end of compute and the scheduler
+      // can interleave its vector work with the last P.V products (C3: -0.9%); after the last tile
+      // it converts a staging stage into an operand stage that nothing reads
+      convert(s81, st1);
       if (t + 3 < n_tiles) {
         copy_tile(t + 3);
         wait_all_but_latest();
