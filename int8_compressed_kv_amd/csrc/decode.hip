@@ -11,31 +11,34 @@
 // O = sum O_s e^(m_s - M) / L, then the epilogue and the store.
 //
 // HBM-bound.  Every K/V byte is read once for all query heads of its group when G <= H (G <= 8
-// at head_dim <= 128, G <= 4 above; a larger group reads the cache ceil(G/H) times).  Each wave streams
-// its own tiles of 32 keys with plain 16-byte vector loads into two register tiles (the next
+// at head_dim <= 128, G <= 4 above; a larger group reads the cache ceil(G/H) times).  Each wave
+// streams its own tiles of 32 keys with 16-byte buffer loads into two register tiles (the next
 // tile is in flight while the current one is computed): on gfx950 this sustains a higher read
 // rate than direct global -> LDS copies.  All cache reads, the per-key scales included, are
 // nontemporal: ordinary cached loads of the small scale vectors interleaved with the streaming
-// code loads measurably lower the achieved read bandwidth.  K is loaded
-// straight into its MFMA operand layout; V passes through a small wave-private LDS slot so
-// that the transposing read can hand each lane 16 keys of one head-dim column.  No barriers
-// are needed until the final combine.
+// code loads measurably lower the achieved read bandwidth.  K is loaded straight into its MFMA
+// operand layout; V passes through a small wave-private LDS slot so that the transposing read
+// can hand each lane 8 keys of one head-dim column.  No barriers are needed until the final
+// combine.  With a group of 8 the wave issues twice the vector work per cache byte at one wave
+// per SIMD, so the per-tile instruction count (loads with loop-invariant offsets, the V^T reads
+// issued ahead of the softmax, DPP sums folded into the adds) sets its speed.
 //
-// Both products run exactly on the int8 MFMA (v_mfma_i32_16x16x64_i8), with no conversion of
-// the cache:
+// Both products run exactly on the int8 MFMA (v_mfma_i32_16x16x64_i8 for Q.K, ..x32_i8 for
+// P~.V), with no conversion of the cache:
 //   * S = Q K^T.  A = K codes (16 keys x 64 head-dim), loaded from global memory.  B holds Q as four signed
 //     7-bit digits, q = 2^E (d0/2^7 + d1/2^14 + d2/2^21 + d3/2^28), one MFMA column per
 //     (digit, head): 4 digits x 4 heads fill the 16 columns that a single decode row would
 //     otherwise leave empty.  The int32 products are exact; the digit columns are recombined
 //     in fp32 with two DPP row rotations, so every lane ends up with the same S.
 //   * O += P~ V with P~ = p * v_s.  x = P~ / 2^F (2^F above every P~ since the last flush) is
-//     rounded to nearest at 28 fractional bits and split into four unsigned 7-bit digits, one
+//     rounded (half up) at 28 fractional bits and split into four unsigned 7-bit digits, one
 //     MFMA column per (digit, head).  A = V^T codes, read with transposing LDS reads
 //     (ds_read_b64_tr_b8) from the row-major tile.  The products accumulate exactly in the
 //     int32 MFMA accumulators across tiles and are moved to fp32 when the running max is raised,
 //     when P~ outgrows 2^F, or after kFlushTiles tiles; F then restarts from the current tile.
-//     Each P~ thus carries an unbiased rounding error of at most 2^(F - 29), F set by the
-//     largest P~ of the tiles since the last flush under the same running max.
+//     Each P~ thus carries a rounding error of at most 2^(F - 29) (or 2^-23 of P~ where
+//     P~ >= 2^(F - 5), below the fp32 rounding P~ already carries), F set by the largest P~ of
+//     the tiles since the last flush under the same running max.
 //   * Key order: MFMA row r of row-block kb holds key (KT/4)(r/4) + 4 kb + r%4, so lane group
 //     g of the score accumulator owns keys (KT/4) g .. (KT/4) g + KT/4 - 1 -- exactly the keys
 //     the transposing read gives that lane group for the P~ V product.
@@ -79,10 +82,13 @@ template <int D>
 struct DCfg {
   static constexpr int KT = 32;                           // keys per tile
   static constexpr int NC16 = D / 16;                     // 16-byte chunks per row
-  static constexpr int SP = (NC16 % 8 == 0) ? 8 : (NC16 % 4 == 0) ? 4 : 2;   // swizzle span
   static constexpr int VCH = KT * NC16 / 64;              // 16-byte V loads per lane per tile
   static constexpr int NSC = 2 * KT / 64;                 // scale values per lane per tile
-  static constexpr int SLOT = KT * D + 8 * KT;            // wave-private LDS bytes (V tile, scales)
+  // LDS row stride of the V slot: 16 bytes of padding per row put the 8 rows that one quarter
+  // of a transposing read touches on distinct banks, and keep every slot address a per-lane
+  // base plus an immediate offset
+  static constexpr int RS = D + 16;
+  static constexpr int SLOT = KT * RS + 8 * KT;           // wave-private LDS bytes (V tile, scales)
   static constexpr int NT = 2;                            // register tile buffers per wave
 };
 
@@ -96,15 +102,13 @@ typedef int i32x2v __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) i32x2v lds_i32x2;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-template <int SP>
-__device__ __forceinline__ int dswz(int r) {
-  return ((r >> 1) ^ (r >> 4)) & (SP - 1);
-}
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kNt = 2;   // nontemporal cache policy of a buffer access
 
 template <int D, int NS, bool SOPS>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeArgs a) {
   using C = DCfg<D>;
-  constexpr int KT = C::KT, NC16 = C::NC16, SP = C::SP, VCH = C::VCH;
+  constexpr int KT = C::KT, NC16 = C::NC16, VCH = C::VCH;
   constexpr int KG = KT / 4;                    // keys per lane group
   constexpr int KB = KT / 16;                   // 16-row blocks of S per tile
   constexpr int NKK = (D + 63) / 64;            // 64-deep k-steps of Q.K
@@ -208,7 +212,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   const int n_tiles_total = (a.s_k - a.key_lo + KT - 1) / KT;
   const int ts = split * a.tiles_per_split;
   const int te = min(n_tiles_total, ts + a.tiles_per_split);
-  const int n_w = te > ts + wave ? (te - ts - wave + kWaves - 1) / kWaves : 0;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int n_w = te > ts + wave_u ? (te - ts - wave_u + kWaves - 1) / kWaves : 0;
   const int last_key = a.s_k - 1;
 
   // ---- register tiles: K in MFMA A layout (row n of block kb = key KG (n/4) + 4 kb + n%4,
@@ -224,39 +229,57 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
   // Per-lane byte offsets inside a tile are loop-invariant; each load is a wave-uniform tile
   // base plus a 32-bit offset, with rows clamped to the last key (only the final tile of the
   // cache has rows past the end; they are masked in compute).
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   int krow_off[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) krow_off[kb] = KG * (n >> 2) + 4 * kb + (n & 3);
+  // Tile loads are raw buffer loads: the resource is the wave-uniform tile base with the bytes
+  // left in the head as its bound, and every per-lane offset is loop-invariant, so a load costs
+  // no vector instruction.  Rows past the last key read zeros (offsets at or beyond the bound);
+  // such keys are masked in compute.  K chunks past head_dim (head_dim not a multiple of 64)
+  // read the next row's bytes, or zeros at the bound: their Q digits are zero.  The scale
+  // lanes that belong to the other matrix get an offset beyond any bound and read zero.
+  constexpr unsigned kOob = 0x80000000u;
+  unsigned koff[KB][NKK], voff[VCH], skoff[NSC], svoff[NSC];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int cidx = 4 * kk + hq;
+      koff[kb][kk] = (unsigned)(krow_off[kb] * D + 16 * cidx);
+    }
+#pragma unroll
+  for (int u = 0; u < VCH; ++u) voff[u] = 16u * (64 * u + lane);
+#pragma unroll
+  for (int e = 0; e < NSC; ++e) {
+    const int slot_i = 64 * e + lane;            // < 2 KT
+    skoff[e] = slot_i < KT ? 4u * slot_i : kOob;
+    svoff[e] = slot_i < KT ? kOob : 4u * (slot_i - KT);
+  }
   auto load = [&](int idx, Tile& T) {
     const int k0 = a.key_lo + (ts + wave_u + kWaves * idx) * KT;
-    const int lim = last_key - k0;                 // last valid row inside this tile
-    const int8_t* kt = a.k + (kv_base + k0) * D;
-    const int8_t* vt = a.v + (kv_base + k0) * D;
+    const int64_t left = a.s_k - k0;             // >= 1: loads never start past the last key
+    const int nrec = (int)min(left * D, (int64_t)0x7fffffff);
+    const int nrec_s = (int)min(left * 4, (int64_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.k + (kv_base + k0) * D), 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.v + (kv_base + k0) * D), 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rks =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.k_scale + kv_base + k0), 0, nrec_s, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rvs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.v_scale + kv_base + k0), 0, nrec_s, kBufferFlags);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int ro = min(krow_off[kb], lim) * D;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int cidx = 4 * kk + hq;
-        T.k[kb][kk] = i32x4{0, 0, 0, 0};
-        if (cidx < NC16) T.k[kb][kk] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kt + ro + 16 * cidx));
-      }
-    }
+      for (int kk = 0; kk < NKK; ++kk)
+        T.k[kb][kk] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[kb][kk], 0, kNt));
 #pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int F = 64 * u + lane;
-      const int o = min(F / NC16, lim) * D + 16 * (F % NC16);
-      T.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + o));
-    }
-    const float* kst = a.k_scale + kv_base + k0;
-    const float* vst = a.v_scale + kv_base + k0;
+    for (int u = 0; u < VCH; ++u)
+      T.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[u], 0, kNt));
 #pragma unroll
-    for (int e = 0; e < NSC; ++e) {
-      const int slot_i = 64 * e + lane;            // < 2 KT
-      const int r = min(slot_i % KT, lim);
-      T.sc[e] = __builtin_nontemporal_load((slot_i < KT ? kst : vst) + r);
-    }
+    for (int e = 0; e < NSC; ++e)
+      T.sc[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, skoff[e], 0, kNt) |
+                                __builtin_amdgcn_raw_buffer_load_b32(rvs, svoff[e], 0, kNt));
   };
   unsigned char* slot = &lds_slot[wave][0];
 
@@ -299,20 +322,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
 
   auto compute = [&](int idx, bool valid, const Tile& T) {
     const int k0 = a.key_lo + (ts + wave_u + kWaves * idx) * KT;
-    // V rows and the scales into the wave's LDS slot (row r, chunk c at chunk c ^ swz(r)), after
-    // the previous tile's reads of it and before this tile's
+    // V rows (row r at r RS) and the scales into the wave's LDS slot, after the previous tile's
+    // reads of it and before this tile's
     wave_lds_order();
 #pragma unroll
     for (int u = 0; u < VCH; ++u) {
       const int Fc = 64 * u + lane;
       const int r = Fc / NC16;
-      *reinterpret_cast<u32x4*>(slot + r * D + 16 * ((Fc % NC16) ^ dswz<SP>(r))) = T.v[u];
+      *reinterpret_cast<u32x4*>(slot + r * C::RS + 16 * (Fc % NC16)) = T.v[u];
     }
 #pragma unroll
-    for (int e = 0; e < NSC; ++e) reinterpret_cast<float*>(slot + KT * D)[64 * e + lane] = T.sc[e];
+    for (int e = 0; e < NSC; ++e) reinterpret_cast<float*>(slot + KT * C::RS)[64 * e + lane] = T.sc[e];
     wave_lds_order();
     const unsigned char* vb_ = slot;
-    const float* sk = reinterpret_cast<const float*>(slot + KT * D);
+    const float* sk = reinterpret_cast<const float*>(slot + KT * C::RS);
     const float* sv = sk + KT;
     // this lane's keys: KG hq + 4 kb + v
     float ks[KB][4], vs[KB][4];
@@ -326,10 +349,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         vs[kb][v] = b4[v];
       }
     }
+    // A = V^T of O^T block b (head-dim 16 b + row), read before the softmax so that the LDS
+    // latency is hidden behind it.  As a source lane, n addresses key row KG hq + n/2, bytes
+    // 16 b + 8 (n%2) .. + 8; lane n then receives keys KG hq + 0..7 of head-dim 16 b + n.
+    static_assert(KG == 8, "P.V takes one 8-key k-group per lane group");
+    long vt[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int vrow = KG * hq + (n >> 1);
+      const int off = vrow * C::RS + 16 * b + 8 * (n & 1);
+      vt[b] = __builtin_bit_cast(long, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)((lds_u8*)vb_ + off)));
+    }
     const bool tail = !valid || k0 + KT > a.s_k;
     const int key_lim = valid ? last_key - k0 - KG * hq : -1;   // key KG hq + j is visible iff j <= key_lim
 
-    i32x4 pdig[NS];
+    long pdig[NS];
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
       // S^T: block kb, C-row 4 hq + v = key KG hq + 4 kb + v; A row n = key KG (n/4) + 4 kb + n%4
@@ -341,7 +375,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         for (int kk = 0; kk < NKK; ++kk) acc = mfma16_i8(T.k[kb][kk], qdig[c][kk], acc);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float y = (float)acc[v] * s_comb[c];
+#pragma clang fp contract(off)
+          float y = (float)acc[v] * s_comb[c];   // kept apart from the add, which then takes the DPP operand
           y = y + dpp_row_ror<8>(y);
           y = y + dpp_row_ror<4>(y);
           s[kb][v] = y * ks[kb][v];
@@ -403,41 +438,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
       if (grow && !raised) flush(c);
       if (raised || grow) F[c] = Fp + 1;          // Oi is empty: restart the scale, one octave of headroom
       ++since_flush[c];
-      // x = P~ / 2^F lies in [0, 1): Q = rint(x 2^28) < 2^28 is x to 28 fractional bits, rounded
-      // to nearest (the scaling by a power of two is exact), and digit t of x is bits
-      // 21 - 7t .. 27 - 7t of Q.  k-slot 4 kb + v of lane group hq is key KG hq + 4 kb + v.
+      // x = P~ / 2^F lies in [0, 1): Q = floor(x 2^28 + 1/2) < 2^28 is x to 28 fractional bits
+      // (one fp32 multiply-add: the scaling by a power of two is exact, and so is the added half
+      // while x 2^28 < 2^23; above, x 2^28 is an integer and the add may round it up by one,
+      // 2^-23 of x at most), and digit t of x is bits 21 - 7t .. 27 - 7t of Q.  k-slot
+      // 4 kb + v of lane group hq is key KG hq + 4 kb + v.
       const int sh = 21 - 7 * t_dig;
-      unsigned pw[4] = {0u, 0u, 0u, 0u};   // k-slots past the tile's keys stay zero
+      unsigned pw[KB];
+      const float sc = ldexpf(1.f, 28 - F[c]);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         unsigned w = 0;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const unsigned qx = (unsigned)__builtin_rintf(ldexpf(pt[kb][v], 28 - F[c]));
-          w |= ((qx >> sh) & 0x7fu) << (8 * v);
+          const unsigned qx = (unsigned)__builtin_fmaf(pt[kb][v], sc, 0.5f);
+          w |= __builtin_amdgcn_ubfe(qx, sh, 7) << (8 * v);
         }
         pw[kb] = w;
       }
-      pdig[c] = i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+      pdig[c] = (long)(((unsigned long)pw[1] << 32) | pw[0]);
     }
 
-    // O^T block b (head-dim 16 b + row): A = V^T via transposing reads, shared by the column
-    // sets.  As a source lane, n addresses key row KG hq + 8 h8 + n/2, bytes 16 b + 8 (n%2) .. + 8;
-    // lane n then receives keys KG hq + 8 h8 + 0..7 of head-dim 16 b + n.
+    // O^T block b += V^T P~^T on the 32-deep int8 MFMA: the tile's 32 keys are its k-slots
+    // (lane group hq holds keys KG hq .. KG hq + 7), V^T is shared by the column sets.
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      int w4[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int h8 = 0; h8 < KG / 8; ++h8) {
-        const int vrow = KG * hq + 8 * h8 + (n >> 1);
-        const int off = vrow * D + 16 * (b ^ dswz<SP>(vrow)) + 8 * (n & 1);
-        const i32x2v r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)((lds_u8*)vb_ + off));
-        w4[2 * h8] = r[0];
-        w4[2 * h8 + 1] = r[1];
-      }
-      const i32x4 vt = {w4[0], w4[1], w4[2], w4[3]};
-#pragma unroll
-      for (int c = 0; c < NS; ++c) Oi[c][b] = mfma16_i8(vt, pdig[c], Oi[c][b]);
+      for (int c = 0; c < NS; ++c) Oi[c][b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(vt[b], pdig[c], Oi[c][b], 0, 0, 0);
     }
   };
 

@@ -36,6 +36,8 @@ namespace {
 constexpr float kTqLazyLog2 = 8.0f;
 constexpr int kTqWaves = 4;
 constexpr int kTqFlushTiles = 1024;   // P~V accumulators: 1024 tiles x 64 keys x 127 x 64 < 2^31
+constexpr int kTqBufferFlags = 0x00020000;
+constexpr int kTqNt = 2;   // nontemporal cache policy of a buffer access
 
 template <int N>
 __device__ __forceinline__ float row_ror(float x) {
@@ -211,9 +213,9 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   const int n_tiles_total = (a.s_k - a.key_lo + KT - 1) / KT;
   const int ts = split * a.tiles_per_split;
   const int te = min(n_tiles_total, ts + a.tiles_per_split);
-  const int n_w = te > ts + wave ? (te - ts - wave + kTqWaves - 1) / kTqWaves : 0;
-  const int last_key = a.s_k - 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int n_w = te > ts + wave_u ? (te - ts - wave_u + kTqWaves - 1) / kTqWaves : 0;
+  const int last_key = a.s_k - 1;
 
   // K: row block kb, lane n is key KG (n/4) + 4 kb + n%4 (so the score accumulator's lane group
   // hq owns keys KG hq .. KG hq + KG - 1, the keys the transposing V reads give it); the lane
@@ -227,38 +229,45 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   int krow[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) krow[kb] = KG * (n >> 2) + 4 * kb + (n & 3);
+  // Raw buffer loads: the resource is the wave-uniform tile base with the bytes left in the head
+  // as its bound and the per-lane offsets are loop-invariant, so a load costs no vector
+  // instruction; rows past the last key read zeros and are masked in compute.
+  unsigned koff[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) koff[kb] = (unsigned)(krow[kb] * RK + hq * QBK);
   auto load = [&](int idx, Tile& T) {
     const int k0 = a.key_lo + (ts + wave_u + kTqWaves * idx) * KT;
-    const int lim = last_key - k0;
-    const uint8_t* kt = a.kc + (kv_base + k0) * RK + hq * QBK;
-    const uint8_t* vt = a.vc + (kv_base + k0) * RV;
+    const int64_t left = a.s_k - k0;             // >= 1: loads never start past the last key
+    const auto rsrc = [&](const void* base, int64_t bytes) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)min(bytes, (int64_t)0x7fffffff),
+                                               kTqBufferFlags);
+    };
+    const __amdgpu_buffer_rsrc_t rk = rsrc(a.kc + (kv_base + k0) * RK, left * RK);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(a.vc + (kv_base + k0) * RV, left * RV);
+    const __amdgpu_buffer_rsrc_t rkn = rsrc(a.kn + kv_base + k0, left * 4);
+    const __amdgpu_buffer_rsrc_t rvn = rsrc(a.vn + kv_base + k0, left * 4);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const uint8_t* p = kt + min(krow[kb], lim) * RK;
       if constexpr (KW % 4 == 0) {
 #pragma unroll
         for (int w4 = 0; w4 < KW / 4; ++w4) {
-          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + w4);
+          const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[kb] + 16 * w4, 0, kTqNt));
 #pragma unroll
           for (int e = 0; e < 4; ++e) T.k[kb][4 * w4 + e] = x[e];
         }
       } else if constexpr (KW == 2) {
-        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, koff[kb], 0, kTqNt));
         T.k[kb][0] = x[0];
         T.k[kb][1] = x[1];
       } else {
-        T.k[kb][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        T.k[kb][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff[kb], 0, kTqNt);
       }
     }
 #pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int F = 64 * u + lane;
-      const int o = min(F / NC16V, lim) * RV + 16 * (F % NC16V);
-      T.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + o));
-    }
-    const int r = min(lane, lim);
-    T.nrm[0] = __builtin_nontemporal_load(a.kn + kv_base + k0 + r);
-    T.nrm[1] = __builtin_nontemporal_load(a.vn + kv_base + k0 + r);
+    for (int u = 0; u < VCH; ++u)
+      T.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16u * (64 * u + lane), 0, kTqNt));
+    T.nrm[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, 4u * lane, 0, kTqNt));
+    T.nrm[1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, 4u * lane, 0, kTqNt));
   };
   unsigned char* slot = &lds_slot[wave][0];
 
@@ -342,8 +351,10 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
       const f32x4 kn = *reinterpret_cast<const f32x4*>(snk + KG * hq + 4 * kb);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float y = __builtin_fmaf((float)acc[2][v], 1.0f / 128.f, (float)acc[1][v]);
-        y = __builtin_fmaf(y, 1.0f / 128.f, (float)acc[0][v]);
+#pragma clang fp contract(off)
+        // digits 1 and 2 joined exactly in int32 (|acc| < 2^20); the multiply stays apart from
+        // the add, which then takes the DPP operand
+        float y = __builtin_fmaf((float)(acc[1][v] * 128 + acc[2][v]), 1.0f / 16384.f, (float)acc[0][v]);
         y *= s_comb;
         y = y + row_ror<8>(y);
         y = y + row_ror<4>(y);
@@ -408,17 +419,19 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
     if (grow && !raised) flush();
     if (raised || grow) F = Fp + 1;
     ++since_flush;
-    // digit t_q of x = P~ / 2^F in [0, 1): bits 21 - 7 t_q .. 27 - 7 t_q of rint(x 2^28); k-slot
-    // 4 kb + v of lane group hq is key KG hq + 4 kb + v
+    // digit t_q of x = P~ / 2^F in [0, 1): bits 21 - 7 t_q .. 27 - 7 t_q of floor(x 2^28 + 1/2),
+    // one fp32 multiply-add (exact while x 2^28 < 2^23; above, x 2^28 is an integer that the add
+    // may raise by one); k-slot 4 kb + v of lane group hq is key KG hq + 4 kb + v
     const int sh = 21 - 7 * t_dig;
+    const float sc = ldexpf(1.f, 28 - F);
     unsigned pw[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       unsigned w = 0;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const unsigned qx = (unsigned)__builtin_rintf(ldexpf(pt[kb][v], 28 - F));
-        w |= ((qx >> sh) & 0x7fu) << (8 * v);
+        const unsigned qx = (unsigned)__builtin_fmaf(pt[kb][v], sc, 0.5f);
+        w |= __builtin_amdgcn_ubfe(qx, sh, 7) << (8 * v);
       }
       pw[kb] = w;
     }
