@@ -153,3 +153,24 @@ def test_decode_group8_reads_the_cache_with_one_workgroup_set():
         out = fa.decode(to_dev(q, "bf16"), *dev, num_splits=splits)
         check_close(to_np(out), ref, TOL_F32, f"G=8 splits={splits}")
         assert fa.last_kernel() == "decode_int8_h8"
+
+
+@pytest.mark.parametrize("d", [32, 96, 128])
+@pytest.mark.parametrize("group", [4, 8])
+def test_decode_tiny_caches_end_at_the_allocation(d, group):
+    """Caches of 1 to 33 keys, so the only (or last) tile runs past the last key of the last KV
+    head, which is the end of the cache allocation: rows past it must read as zeros and be
+    masked.  At head_dim 32 and 96 some lanes' K chunks lie past the row (their Q digits are
+    zero); the last row's overhang is past the allocation too."""
+    import int8_compressed_kv_amd as fa
+    torch_gpu()
+    for s_k in (1, 7, 31, 32, 33):
+        say(f"decode tiny d={d} G={group} s_k={s_k}")
+        q, k, v = rng_normal(720 + s_k + d, (2 * group, 1, d), (2, s_k, d), (2, s_k, d))
+        q = round_bf16(q)
+        dev, (kq, ks, vq, vs) = _cache(k, v)
+        ref, lref = oracle.decode(q, kq, vq, k_scale=ks, v_scale=vs)
+        for splits in (0, 1, 3):
+            out, lse = fa.decode(to_dev(q, "bf16"), *dev, num_splits=splits, return_lse=True)
+            check_close(to_np(out), ref, TOL_F32, f"d={d} G={group} s_k={s_k} splits={splits}")
+            check_close(to_np(lse), lref[:, 0], TOL_F32, "lse")
