@@ -496,9 +496,10 @@ int32_t fa_tq_attention_num_splits(int32_t bh_q, int32_t bh_kv, int32_t s_k, int
   const int32_t group = bh_q / bh_kv;
   const int64_t units = (int64_t)bh_kv * ((group + 3) / 4);
   const int32_t tiles = (s_k + kTqAttnTile - 1) / kTqAttnTile;
-  // about 1024 workgroups (two fit on a CU at once, and the surplus evens out the tail), each
-  // split keeping at least 8 tiles (2 per wave)
-  int64_t splits = (1024 + units - 1) / units;
+  // about 512 workgroups (two fit on a CU at once; more splits spread each workgroup's start, the
+  // q rotation and digit split, over fewer tiles: 152 against 150 us at 8 and 4 splits per KV
+  // head on the long-cache shape), each split keeping at least 8 tiles (2 per wave)
+  int64_t splits = (512 + units - 1) / units;
   const int64_t max_by_len = tiles / 8 > 0 ? tiles / 8 : 1;
   if (splits > max_by_len) splits = max_by_len;
   if (splits > kMaxSplits) splits = kMaxSplits;

@@ -48,6 +48,26 @@ typedef int i32x2t __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) i32x2t lds_i32x2t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8t;
 
+// In-place unnormalised Walsh-Hadamard transform of `rows` contiguous LDS vectors of length D
+// (Sylvester order: y_r = sum_j (-1)^popcount(r & j) x_j), by threads t = 0 .. n-1 of the block:
+// log2(D) butterfly stages (a, b) -> (a + b, a - b) over index bit h, one pair per thread and
+// step, a barrier after each stage (the last one included, so x is ready on return).
+template <int D>
+__device__ __forceinline__ void lds_hadamard(float* x, int rows, int t, int n) {
+  static_assert((D & (D - 1)) == 0, "Hadamard length is a power of two");
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1) {
+    for (int p = t; p < rows * (D / 2); p += n) {
+      const int k = p % (D / 2);
+      const int lo = (p / (D / 2)) * D + (k / h) * 2 * h + k % h;
+      const float u = x[lo], w = x[lo + h];
+      x[lo] = u + w;
+      x[lo + h] = u - w;
+    }
+    __syncthreads();
+  }
+}
+
 // Byte lookups of four code bytes (one code per byte, values below 2^BITS) in a digit table.
 template <int BITS>
 __device__ __forceinline__ unsigned lookup4(unsigned sel, const uint32_t (&tab)[4]) {
@@ -139,26 +159,7 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
     lds_q[g][j] = x;
   }
   __syncthreads();
-  constexpr int QR = HPW * D / (64 * kTqWaves);   // q' entries per thread
-  float qp[QR];
-#pragma unroll
-  for (int r = 0; r < QR; ++r) {
-    const int i = tid + 64 * kTqWaves * r;
-    const int g = i / D, row = i % D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) {
-      const float v = lds_q[g][j];
-      acc += (__popc(row & j) & 1) ? -v : v;
-    }
-    qp[r] = acc;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < QR; ++r) {
-    const int i = tid + 64 * kTqWaves * r;
-    lds_q[i / D][i % D] = qp[r];
-  }
-  __syncthreads();
+  lds_hadamard<D>(&lds_q[0][0], HPW, tid, 64 * kTqWaves);
 
   // ---- q' digit B operands (column n = (t_dig, gq), k-slots in the K lookup order)
   i32x4 qdig[NKK];
@@ -520,8 +521,8 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   }
 }
 
-// Pass 2: one workgroup of 64 lanes per query head.  The merged O' / L goes through LDS and each
-// lane forms its outputs x_i = s_V[i] sum_j H[i][j] O'_j / sqrt(d).
+// Pass 2: one workgroup of 64 lanes per query head.  The merged O' / L goes through LDS, where a
+// Walsh-Hadamard transform forms H O'; the outputs are x_i = s_V[i] (H O')_i / sqrt(d).
 template <int D>
 __global__ __launch_bounds__(64) void tq_attn_merge_kernel(TqAttnArgs a) {
   constexpr int PER = D / 64;
@@ -553,17 +554,13 @@ __global__ __launch_bounds__(64) void tq_attn_merge_kernel(TqAttnArgs a) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) o_rot[lane + 64 * e] = o[e] * inv;
   __syncthreads();
+  lds_hadamard<D>(o_rot, 1, lane, 64);
   const float rs = 1.0f / sqrtf((float)D);
   float y[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int i = lane + 64 * e;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) {
-      const float v = o_rot[j];
-      acc += (__popc(i & j) & 1) ? -v : v;
-    }
-    acc *= rs;
+    const float acc = o_rot[i] * rs;
     y[e] = a.vs[i] < 0 ? -acc : acc;
   }
   apply_epilogue_all(y, a.epi, [&](int e) { return lane + 64 * e; });
