@@ -363,11 +363,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
     const bool tail = !valid || k0 + KT > a.s_k;
     const int key_lim = valid ? last_key - k0 - KG * hq : -1;   // key KG hq + j is visible iff j <= key_lim
 
-    long pdig[NS];
+    // The column sets go through each phase of the tile together: the rare raise and flush
+    // branches then split the code only between phases, and within a phase the sets' independent
+    // instructions interleave (one wave per SIMD has no other wave to cover their latencies).
+    // S^T: block kb, C-row 4 hq + v = key KG hq + 4 kb + v; A row n = key KG (n/4) + 4 kb + n%4
+    float s[NS][KB][4];
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
-      // S^T: block kb, C-row 4 hq + v = key KG hq + 4 kb + v; A row n = key KG (n/4) + 4 kb + n%4
-      float s[KB][4];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         i32x4 acc = {0, 0, 0, 0};
@@ -379,35 +381,45 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
           float y = (float)acc[v] * s_comb[c];   // kept apart from the add, which then takes the DPP operand
           y = y + dpp_row_ror<8>(y);
           y = y + dpp_row_ror<4>(y);
-          s[kb][v] = y * ks[kb][v];
+          s[c][kb][v] = y * ks[kb][v];
         }
       }
       if constexpr (SOPS) {
         float x[KB * 4];
 #pragma unroll
-        for (int j = 0; j < KB * 4; ++j) x[j] = s[j / 4][j % 4];
+        for (int j = 0; j < KB * 4; ++j) x[j] = s[c][j / 4][j % 4];
         apply_score_ops(x, a.sops, [&](int j) { return min(k0 + KG * hq + j, last_key); });
 #pragma unroll
-        for (int j = 0; j < KB * 4; ++j) s[j / 4][j % 4] = x[j];
+        for (int j = 0; j < KB * 4; ++j) s[c][j / 4][j % 4] = x[j];
       }
-      if (tail) {
+    }
+    if (tail) {
+#pragma unroll
+      for (int c = 0; c < NS; ++c)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (4 * kb + v > key_lim) s[kb][v] = neg_inf();
-      }
-      float mx = neg_inf();
+            if (4 * kb + v > key_lim) s[c][kb][v] = neg_inf();
+    }
+    float mx[NS];
+    bool raised[NS];   // wave-uniform
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      float m = neg_inf();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = max_xor16(mx);
-      mx = max_xor32(mx);
-      const bool raised = __any(mx - m_run[c] > lazy_thr);   // wave-uniform
-      if (raised) {
+        for (int v = 0; v < 4; ++v) m = fmaxf(m, s[c][kb][v]);
+      m = max_xor16(m);
+      mx[c] = max_xor32(m);
+      raised[c] = __any(mx[c] - m_run[c] > lazy_thr);
+    }
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      if (raised[c]) {
         flush(c);
-        const float m_new = fmaxf(m_run[c], mx);
+        const float m_new = fmaxf(m_run[c], mx[c]);
         const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f((m_run[c] - m_use) * c2);
         l_run[c] *= alpha;
@@ -418,32 +430,44 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         m_run[c] = m_new;
         mc[c] = m_use * c2;
       }
-      float pt[KB][4];
+    }
+    float pt[NS][KB][4];
+    int Fp[NS];
+    bool grow[NS];     // wave-uniform
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
       float ps = 0.f, pmax = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], c2, -mc[c]));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][kb][v], c2, -mc[c]));
           ps += p;
-          pt[kb][v] = p * vs[kb][v];
-          pmax = fmaxf(pmax, pt[kb][v]);
+          pt[c][kb][v] = p * vs[kb][v];
+          pmax = fmaxf(pmax, pt[c][kb][v]);
         }
       l_run[c] += ps;
       pmax = max_xor16(pmax);
       pmax = max_xor32(pmax);
-      int Fp = -1000;
-      if (pmax > 0.f) (void)frexpf(pmax, &Fp);    // pmax < 2^Fp
-      const bool grow = __any(Fp > F[c]) || since_flush[c] >= kFlushTiles;   // wave-uniform
-      if (grow && !raised) flush(c);
-      if (raised || grow) F[c] = Fp + 1;          // Oi is empty: restart the scale, one octave of headroom
+      Fp[c] = -1000;
+      if (pmax > 0.f) (void)frexpf(pmax, &Fp[c]);    // pmax < 2^Fp
+      grow[c] = __any(Fp[c] > F[c]) || since_flush[c] >= kFlushTiles;
+    }
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      if (grow[c] && !raised[c]) flush(c);
+      if (raised[c] || grow[c]) F[c] = Fp[c] + 1;   // Oi is empty: restart the scale, one octave of headroom
       ++since_flush[c];
-      // x = P~ / 2^F lies in [0, 1): Q = floor(x 2^28 + 1/2) < 2^28 is x to 28 fractional bits
-      // (one fp32 multiply-add: the scaling by a power of two is exact, and so is the added half
-      // while x 2^28 < 2^23; above, x 2^28 is an integer and the add may round it up by one,
-      // 2^-23 of x at most), and digit t of x is bits 21 - 7t .. 27 - 7t of Q.  k-slot
-      // 4 kb + v of lane group hq is key KG hq + 4 kb + v.
-      const int sh = 21 - 7 * t_dig;
+    }
+    // x = P~ / 2^F lies in [0, 1): Q = floor(x 2^28 + 1/2) < 2^28 is x to 28 fractional bits
+    // (one fp32 multiply-add: the scaling by a power of two is exact, and so is the added half
+    // while x 2^28 < 2^23; above, x 2^28 is an integer and the add may round it up by one,
+    // 2^-23 of x at most), and digit t of x is bits 21 - 7t .. 27 - 7t of Q.  k-slot
+    // 4 kb + v of lane group hq is key KG hq + 4 kb + v.
+    const int sh = 21 - 7 * t_dig;
+    long pdig[NS];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
       unsigned pw[KB];
       const float sc = ldexpf(1.f, 28 - F[c]);
 #pragma unroll
@@ -451,7 +475,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_partial_kernel(DecodeAr
         unsigned w = 0;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const unsigned qx = (unsigned)__builtin_fmaf(pt[kb][v], sc, 0.5f);
+          const unsigned qx = (unsigned)__builtin_fmaf(pt[c][kb][v], sc, 0.5f);
           w |= __builtin_amdgcn_ubfe(qx, sh, 7) << (8 * v);
         }
         pw[kb] = w;
