@@ -521,6 +521,8 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   }
 }
 
+constexpr int kTqMergeBatch = 8;   // splits whose partial states are loaded together
+
 // Pass 2: one workgroup of 64 lanes per query head.  The merged O' / L goes through LDS, where a
 // Walsh-Hadamard transform forms H O'; the outputs are x_i = s_V[i] (H O')_i / sqrt(d).
 template <int D>
@@ -532,22 +534,38 @@ __global__ __launch_bounds__(64) void tq_attn_merge_kernel(TqAttnArgs a) {
   const float c2 = a.scale_log2;
   const int S = a.num_splits;
   const float* p = a.partial + (int64_t)head * S * (D + 2);
-  float M = neg_inf();
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, p[(int64_t)s * (D + 2)]);
-#pragma unroll
-  for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
-  float L = 0.f;
+  // The partial states of up to kTqMergeBatch splits are loaded before any of them is used (one
+  // memory round trip for the usual few splits); a later batch rescales what came before.
+  float M = neg_inf(), L = 0.f;
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  if (M != neg_inf()) {
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) {
-      const float* ps = p + (int64_t)s * (D + 2);
-      const float w = __builtin_amdgcn_exp2f((ps[0] - M) * c2);
-      L += w * ps[1];
+  for (int s0 = 0; s0 < S; s0 += kTqMergeBatch) {
+    float ms[kTqMergeBatch], ls[kTqMergeBatch], os[kTqMergeBatch][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] += w * ps[2 + lane + 64 * e];
+    for (int j = 0; j < kTqMergeBatch; ++j) {
+      const float* ps = p + (int64_t)min(s0 + j, S - 1) * (D + 2);
+      ms[j] = s0 + j < S ? ps[0] : neg_inf();
+      ls[j] = ps[1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) os[j][e] = ps[2 + min(lane + 64 * e, D - 1)];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kTqMergeBatch; ++j) Mb = fmaxf(Mb, ms[j]);
+    if (Mb != neg_inf()) {
+      const float r = __builtin_amdgcn_exp2f((M - Mb) * c2);   // 0 while M is -inf
+      L *= r;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] *= r;
+#pragma unroll
+      for (int j = 0; j < kTqMergeBatch; ++j) {
+        const float w = __builtin_amdgcn_exp2f((ms[j] - Mb) * c2);
+        L += w * ls[j];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] += w * os[j][e];
+      }
+      M = Mb;
     }
   }
   const float inv = L > 0.f ? __fdiv_rn(1.0f, L) : 0.f;
