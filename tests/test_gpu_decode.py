@@ -90,7 +90,7 @@ def test_decode_split_count_independence_and_determinism():
     q, k, v = rng_normal(603, (16, 1, 128), (4, 9000, 128), (4, 9000, 128))
     q = round_bf16(q)
     dev, _ = _cache(k, v)
-    outs = [to_np(fa.decode(to_dev(q, "bf16"), *dev, num_splits=s)) for s in (1, 2, 5, 32)]
+    outs = [to_np(fa.decode(to_dev(q, "bf16"), *dev, num_splits=s)) for s in (1, 2, 5, 13, 32)]
     for o in outs[1:]:
         check_close(o, outs[0].astype(np.float64), 2e-6, "split independence")
     a = fa.decode(to_dev(q, "bf16"), *dev, num_splits=5)

@@ -49,7 +49,7 @@ def test_tq_attention_matches_oracle_on_the_same_codes(d, kb, vb):
     q = round_bf16(q)
     dev, host = _coded_cache(k, v, kb, vb, 2100 + d)
     ref, lref = _ref(q, host)
-    for splits in (0, 1, 5):
+    for splits in (0, 1, 5, 20):   # 20: several merge batches of 8 splits, some splits empty
         out, lse = fa.tq_attention_decode(to_dev(q, "bf16"), *dev, num_splits=splits, return_lse=True)
         check_close(to_np(out), ref, TOL_F32, f"d={d} K{kb}/V{vb} splits={splits}")
         check_close(to_np(lse), lref[:, 0], TOL_F32, "lse")
