@@ -15,6 +15,7 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   tq     TurboQuant 4-bit encode of the c4 K cache (fp32 in) and decode of it back to bf16
   tqattn decode attention read straight from TurboQuant codes of the c4 cache (K 4-bit, V 2-bit,
          the page's default), 16 x 32 query / 8 KV heads, 32768 keys, d 128
+  tqattn33 (not in the default set) the same with 3-bit K and V codes, which straddle bytes
   merge  log-sum-exp merge of 8 key-chunk results for one 4096-row query chunk of the c5 shape
          (64 heads x 4096 rows, d 128, fp32 parts, bf16 output): the exchange of a ring prefill
   copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
@@ -67,6 +68,7 @@ LEG_SOURCES = {
     "tq": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
     "tq_dec": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
     "tqattn": ("tq_attn.hip", "device_common.hpp", "kernel_args.hpp"),
+    "tqattn33": ("tq_attn.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
@@ -266,7 +268,7 @@ def main():
         del qd, kc, ks, vc, vs, out, q, k, v
 
     # ------------------------------------------------------------------ compress + decode c4
-    if legs & {"c4", "c4g8", "comp", "append", "tq", "tqattn"}:
+    if legs & {"c4", "c4g8", "comp", "append", "tq", "tqattn", "tqattn33"}:
         w = WORKLOADS["c4"]
         log(f"[bench] generating {w.name}")
         q, k, v = draw_qkv(w)
@@ -314,9 +316,10 @@ def main():
                              "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] tq decode: {avg:.3f} ms  {res['tq_dec']['gbs']:.0f} GB/s")
             del codes, norms, kb16, signs
-        if "tqattn" in legs:
+        for tq_leg, kbits, vbits in (("tqattn", 4, 2), ("tqattn33", 3, 3)):
+            if tq_leg not in legs:
+                continue
             from synth_inputs import random_signs
-            kbits, vbits = 4, 2
             kcb, vcb = fa.tq_codebook(w.d, kbits), fa.tq_codebook(w.d, vbits)
             sk = torch.from_numpy(random_signs(64, w.d)).cuda()
             sv = torch.from_numpy(random_signs(65, w.d)).cuda()
@@ -328,15 +331,15 @@ def main():
                                dtype=torch.uint8, device="cuda")
             fn = lambda: fa.tq_attention_decode(qd, kcode, kn, sk, kbits, kcb, vcode, vn, sv, vbits, vcb,   # noqa: E731
                                                 num_splits=splits_t, out=out_t, workspace=ws_t)
-            log("[bench] timing decode attention over TurboQuant codes (K4/V2, c4 shape)")
+            log(f"[bench] timing decode attention over TurboQuant codes (K{kbits}/V{vbits}, c4 shape)")
             ms = timer.run(fn, args.steps, args.warmup, flush=flush)
             avg = float(np.mean(ms))
             nbytes = n_tok * (w.d * kbits // 8 + 4 + w.d * vbits // 8 + 4) + w.bh_q * w.d * 2 + w.bh_q * w.d * 4
-            res["tqattn"] = {"workload": "tq_attention_decode_k4v2_b16_h32kv8_sk32768_d128", "ms": avg,
-                             "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "num_splits": splits_t,
-                             "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
-                             "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
-            log(f"[bench] tqattn: {avg * 1e3:.1f} us  {res['tqattn']['gbs']:.0f} GB/s")
+            res[tq_leg] = {"workload": f"tq_attention_decode_k{kbits}v{vbits}_b16_h32kv8_sk32768_d128", "ms": avg,
+                           "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "num_splits": splits_t,
+                           "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
+                           "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
+            log(f"[bench] {tq_leg}: {avg * 1e3:.1f} us  {res[tq_leg]['gbs']:.0f} GB/s")
             del kcode, kn, vcode, vn, out_t, ws_t, sk, sv
         fa.compress_kv(kf, kc, ks)
         fa.compress_kv(vf, vc, vs)

@@ -246,7 +246,9 @@ int fa_tq_decode(const uint8_t* codes, const float* norms, int64_t n_tokens, int
  *   k_codes    device uint8 [bh_kv, s_k, head_dim k_bits / 8] as fa_tq_encode writes them;
  *              k_norms device fp32 [bh_kv, s_k]; k_signs device int8 [head_dim]; k_codebook host
  *              fp32 [2^k_bits], strictly increasing; likewise for V.
- *   k_bits, v_bits  2 or 4.  head_dim 64 or 128.
+ *   k_bits, v_bits  2, 3 or 4 (3-bit codes straddle bytes in the packed stream; the kernel
+ *                   widens each 24-bit run of 8 codes to 4-bit fields in registers).
+ *                   head_dim 64 or 128.
  *   out, lse_out, softmax_scale, window, num_splits, epi, workspace: as for fa_decode, with
  *              fa_tq_attention_num_splits / fa_tq_attention_workspace_bytes for the sizes.
  * The codebooks enter as three 7-bit digits each (2^-22 of their largest entry); all other

@@ -524,8 +524,8 @@ int fa_tq_attention_decode(const void* q, int32_t q_dtype, const uint8_t* k_code
   g_last_error.clear();
   if (head_dim != 64 && head_dim != 128)
     return fail(FA_ERR_UNSUPPORTED, "TurboQuant attention needs head_dim 64 or 128 (got %d)", head_dim);
-  if ((k_bits != 2 && k_bits != 4) || (v_bits != 2 && v_bits != 4))
-    return fail(FA_ERR_UNSUPPORTED, "TurboQuant attention reads 2- or 4-bit codes (got K %d, V %d)", k_bits, v_bits);
+  if (k_bits < 2 || k_bits > 4 || v_bits < 2 || v_bits > 4)
+    return fail(FA_ERR_UNSUPPORTED, "TurboQuant attention reads 2-, 3- or 4-bit codes (got K %d, V %d)", k_bits, v_bits);
   if (bh_q <= 0 || bh_kv <= 0) return fail(FA_ERR_INVALID, "bh_q and bh_kv must be positive");
   if (bh_q % bh_kv != 0) return fail(FA_ERR_INVALID, "bh_q (%d) must be a multiple of bh_kv (%d)", bh_q, bh_kv);
   if (s_k < 0) return fail(FA_ERR_INVALID, "s_k must be >= 0");

@@ -14,8 +14,11 @@
 // Both products run on the int8 MFMA (v_mfma_i32_16x16x64_i8) in the digit form of the int8
 // decode:
 //   * codebook entries as three signed 7-bit digits of c 2^-E, looked up per byte with v_perm_b32
-//     from 16-byte digit tables (4 entries for 2-bit codes: one permute; 16 entries for 4-bit
-//     codes: two permutes and a byte select);
+//     from 16-byte digit tables (4 entries for 2-bit codes and 8 for 3-bit codes: one permute;
+//     16 entries for 4-bit codes: two permutes and a byte select);
+//   * 3-bit codes, which straddle bytes in the packed stream, are first widened in registers to
+//     the 4-bit layout (each 24-bit run of 8 codes becomes one 32-bit word of nibbles), so both
+//     products then read them exactly as 4-bit codes whose values stay below 8;
 //   * q' as four signed 7-bit digits under a per-head power of two (B of S = K q'), and
 //     P~_j = p_j n^V_j as four unsigned 7-bit digits of P~ / 2^F rounded at 28 bits (B of
 //     O' += V^T P~), one MFMA column per (digit, head) for 4 heads;
@@ -73,6 +76,8 @@ template <int BITS>
 __device__ __forceinline__ unsigned lookup4(unsigned sel, const uint32_t (&tab)[4]) {
   if constexpr (BITS == 2) {
     return __builtin_amdgcn_perm(tab[0], tab[0], sel);                 // selectors 0..3: entries 0..3
+  } else if constexpr (BITS == 3) {
+    return __builtin_amdgcn_perm(tab[1], tab[0], sel);                 // selectors 0..7: entries 0..7
   } else {
     const unsigned s7 = sel & 0x07070707u;
     const unsigned lo = __builtin_amdgcn_perm(tab[1], tab[0], s7);     // entries 0..7
@@ -82,24 +87,42 @@ __device__ __forceinline__ unsigned lookup4(unsigned sel, const uint32_t (&tab)[
   }
 }
 
+// The 8 three-bit fields in bits 0..23 of x (field k at bits 3k .. 3k + 2; bits 24..31 are
+// ignored) as the 8 nibbles of a word (field k at bits 4k .. 4k + 2, bit 4k + 3 clear): three
+// shift-and-merge steps, each moving half of the fields of every group by one more place.
+__device__ __forceinline__ unsigned widen3to4(unsigned x) {
+  const unsigned y = (x & 0x0000ffffu) | ((x << 4) & 0xffff0000u);     // fields 4..7 to bit 16
+  const unsigned y2 = (y & 0x003f003fu) | ((y << 2) & 0xffc0ffc0u);    // fields 2, 3 (6, 7) up by 2
+  const unsigned z = (y2 & 0x0f0f0f0fu) | ((y2 << 1) & 0xf0f0f0f0u);   // fields 1, 3, 5, 7 up by 1
+  return z & 0x77777777u;
+}
+
 template <int D, int KBITS, int VBITS>
 struct TqCfg {
   static constexpr int KT = 64;                       // keys per tile
   static constexpr int KG = 16;                       // keys per lane group
   static constexpr int NKB = KT / 16;                 // 16-key row blocks of S
   static constexpr int NKK = D / 64;                  // 64-deep k-steps of S
-  static constexpr int RK = D * KBITS / 8;            // K code bytes per key
-  static constexpr int QBK = RK / 4;                  // K code bytes per lane group and key
+  static constexpr int LK = KBITS == 3 ? 4 : KBITS;   // code width of the register layout
+  static constexpr int LV = VBITS == 3 ? 4 : VBITS;   // ... and of the LDS layout (3 bits widened)
+  static constexpr int RKS = D * KBITS / 8;           // K code bytes per key in memory
+  static constexpr int RVS = D * VBITS / 8;           // V code bytes per key in memory
+  static constexpr int RK = D * LK / 8;               // K code bytes per key, register layout
+  static constexpr int QBK = RK / 4;                  // ... per lane group and key
   static constexpr int KW = QBK / 4;                  // ... as 32-bit words
-  static constexpr int RV = D * VBITS / 8;            // V code bytes per key
+  static constexpr int QBK3 = 3 * D / 32;             // 3-bit K: bytes per lane group and key
+  static constexpr int NW3 = D == 64 ? 2 : QBK3 / 4;  // 3-bit K: words loaded per row block
+  static constexpr int NV3 = RVS / 4;                 // 3-bit V: words of one key row
+  static constexpr int RV = D * LV / 8;               // V code bytes per key, LDS layout
   static constexpr int NC16V = RV / 16;               // 16-byte chunks per V row
   static constexpr int VCH = KT * NC16V / 64;         // 16-byte V loads per lane per tile
-  static constexpr int FV = 8 / VBITS;                // codes per V byte
+  static constexpr int FV = 8 / LV;                   // codes per V byte (LDS layout)
   static constexpr int NBLK = NC16V * FV;             // 16-channel blocks of O' (= D / 16)
   static constexpr int SP = NC16V >= 8 ? 8 : NC16V >= 4 ? 4 : NC16V >= 2 ? 2 : 1;   // LDS swizzle span
   static constexpr int SLOT = KT * RV + 8 * KT;       // wave-private LDS bytes (V tile, norms)
   static_assert(NBLK == D / 16, "block count");
   static_assert(QBK % 4 == 0 && NC16V >= 1, "layout");
+  static_assert((D == 64 || D == 128) && (QBK3 % 4 == 0 || D == 64), "3-bit row pieces");
 };
 
 template <int SP>
@@ -114,16 +137,18 @@ template <int D, int KBITS>
 __device__ __forceinline__ int k_slot_channel(int kk, int hq, int s) {
   const int base = hq * (D / 4) + 16 * kk;
   const int w = s >> 2, e = s & 3;
-  if constexpr (KBITS == 4) return base + 8 * (w >> 1) + 2 * e + (w & 1);
+  if constexpr (KBITS >= 3) return base + 8 * (w >> 1) + 2 * e + (w & 1);   // 3 bits: widened to 4
   else return base + 4 * e + w;
 }
 
 template <int D, int KBITS, int VBITS, bool SOPS>
-__global__ __launch_bounds__(64 * kTqWaves, (D == 128 && KBITS == 4 && VBITS == 4) ? 1 : 2)   // 4/4 needs > 256 VGPRs
+__global__ __launch_bounds__(64 * kTqWaves, (D == 128 && KBITS == 4 && VBITS >= 3) ? 1 : 2)   // 4/4 needs > 256 VGPRs
 void tq_attn_partial_kernel(TqAttnArgs a) {
   using C = TqCfg<D, KBITS, VBITS>;
   constexpr int KT = C::KT, KG = C::KG, NKB = C::NKB, NKK = C::NKK, RK = C::RK, QBK = C::QBK, KW = C::KW;
   constexpr int RV = C::RV, NC16V = C::NC16V, VCH = C::VCH, FV = C::FV, NBLK = C::NBLK, SP = C::SP;
+  constexpr int RKS = C::RKS, RVS = C::RVS, QBK3 = C::QBK3, NW3 = C::NW3, NV3 = C::NV3;
+  constexpr bool K3 = KBITS == 3, V3 = VBITS == 3;
   constexpr int HPW = 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds_slot[kTqWaves][C::SLOT];
@@ -222,9 +247,12 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   // hq owns keys KG hq .. KG hq + KG - 1, the keys the transposing V reads give it); the lane
   // loads its group's QBK bytes of that row.  V: 16-byte chunk F = 64 u + lane of the tile's
   // contiguous rows.  Norms: entry 64 e + lane of [K norms | V norms].
+  // 3-bit codes: K rows as the lane group's packed words (widened in compute), V rows one key per
+  // lane as packed words (widened into the LDS slot in compute).
   struct Tile {
-    uint32_t k[NKB][KW];
-    u32x4 v[VCH];
+    uint32_t k[NKB][K3 ? NW3 : KW];
+    u32x4 v[V3 ? 1 : VCH];
+    uint32_t v3[V3 ? NV3 : 1];
     float nrm[2];
   };
   int krow[NKB];
@@ -233,9 +261,14 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   // Raw buffer loads: the resource is the wave-uniform tile base with the bytes left in the head
   // as its bound and the per-lane offsets are loop-invariant, so a load costs no vector
   // instruction; rows past the last key read zeros and are masked in compute.
+  // 3-bit K: the lane group's QBK3 bytes start at byte hq QBK3 of the row, which is 4-byte aligned
+  // except at head_dim 64 (6 bytes per group): there the load starts at the aligned word below and
+  // the run is shifted down by sh3 bits (the last group's load still ends at the row's end).
   unsigned koff[NKB];
+  const unsigned sh3 = K3 ? (unsigned)((hq * QBK3) & 3) * 8u : 0u;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) koff[kb] = (unsigned)(krow[kb] * RK + hq * QBK);
+  for (int kb = 0; kb < NKB; ++kb)
+    koff[kb] = K3 ? (unsigned)(krow[kb] * RKS + ((hq * QBK3) & ~3)) : (unsigned)(krow[kb] * RK + hq * QBK);
   auto load = [&](int idx, Tile& T) {
     const int k0 = a.key_lo + (ts + wave_u + kTqWaves * idx) * KT;
     const int64_t left = a.s_k - k0;             // >= 1: loads never start past the last key
@@ -243,13 +276,23 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)min(bytes, (int64_t)0x7fffffff),
                                                kTqBufferFlags);
     };
-    const __amdgpu_buffer_rsrc_t rk = rsrc(a.kc + (kv_base + k0) * RK, left * RK);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(a.vc + (kv_base + k0) * RV, left * RV);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(a.kc + (kv_base + k0) * RKS, left * RKS);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(a.vc + (kv_base + k0) * RVS, left * RVS);
     const __amdgpu_buffer_rsrc_t rkn = rsrc(a.kn + kv_base + k0, left * 4);
     const __amdgpu_buffer_rsrc_t rvn = rsrc(a.vn + kv_base + k0, left * 4);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      if constexpr (KW % 4 == 0) {
+      if constexpr (K3 && NW3 == 3) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b96(rk, koff[kb], 0, kTqNt);
+        T.k[kb][0] = (uint32_t)x[0];
+        T.k[kb][1] = (uint32_t)x[1];
+        T.k[kb][2] = (uint32_t)x[2];
+      } else if constexpr (K3) {
+        static_assert(NW3 == 2, "3-bit K run");
+        const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, koff[kb], 0, kTqNt));
+        T.k[kb][0] = x[0];
+        T.k[kb][1] = x[1];
+      } else if constexpr (KW % 4 == 0) {
 #pragma unroll
         for (int w4 = 0; w4 < KW / 4; ++w4) {
           const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[kb] + 16 * w4, 0, kTqNt));
@@ -264,9 +307,25 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
         T.k[kb][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff[kb], 0, kTqNt);
       }
     }
+    if constexpr (V3 && RVS % 16 == 0) {
 #pragma unroll
-    for (int u = 0; u < VCH; ++u)
-      T.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16u * (64 * u + lane), 0, kTqNt));
+      for (int u = 0; u < RVS / 16; ++u) {
+        const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, RVS * lane + 16 * u, 0, kTqNt));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) T.v3[4 * u + e] = x[e];
+      }
+    } else if constexpr (V3) {
+#pragma unroll
+      for (int u = 0; u < RVS / 8; ++u) {
+        const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, RVS * lane + 8 * u, 0, kTqNt));
+        T.v3[2 * u] = x[0];
+        T.v3[2 * u + 1] = x[1];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VCH; ++u)
+        T.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16u * (64 * u + lane), 0, kTqNt));
+    }
     T.nrm[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rkn, 4u * lane, 0, kTqNt));
     T.nrm[1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvn, 4u * lane, 0, kTqNt));
   };
@@ -309,11 +368,23 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
     // V codes and the norms into the wave's LDS slot, after the previous tile's reads of it and
     // before this tile's
     wave_lds_order();
+    if constexpr (V3) {
+      // lane = key row: every 3 packed words hold 4 runs of 8 codes, each widened to a word of
+      // nibbles, so the slot row is the row's 4-bit layout
 #pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int Fc = 64 * u + lane;
-      const int r = Fc / NC16V;
-      *reinterpret_cast<u32x4*>(slot + r * RV + 16 * ((Fc % NC16V) ^ tswz<SP>(r))) = T.v[u];
+      for (int j = 0; j < NC16V; ++j) {
+        const unsigned a0 = T.v3[3 * j], a1 = T.v3[3 * j + 1], a2 = T.v3[3 * j + 2];
+        const u32x4 w = {widen3to4(a0), widen3to4(__builtin_amdgcn_alignbit(a1, a0, 24)),
+                         widen3to4(__builtin_amdgcn_alignbit(a2, a1, 16)), widen3to4(a2 >> 8)};
+        *reinterpret_cast<u32x4*>(slot + lane * RV + 16 * (j ^ tswz<SP>(lane))) = w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VCH; ++u) {
+        const int Fc = 64 * u + lane;
+        const int r = Fc / NC16V;
+        *reinterpret_cast<u32x4*>(slot + r * RV + 16 * ((Fc % NC16V) ^ tswz<SP>(r))) = T.v[u];
+      }
     }
     reinterpret_cast<float*>(slot + KT * RV)[lane] = T.nrm[0];
     reinterpret_cast<float*>(slot + KT * RV)[64 + lane] = T.nrm[1];
@@ -328,17 +399,33 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       i32x4 acc[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+      // the row block's code words in the 4-bit register layout (3-bit runs widened)
+      uint32_t kw[KW];
+      if constexpr (K3 && NW3 == 3) {
+        const unsigned a0 = T.k[kb][0], a1 = T.k[kb][1], a2 = T.k[kb][2];
+        kw[0] = widen3to4(a0);
+        kw[1] = widen3to4(__builtin_amdgcn_alignbit(a1, a0, 24));
+        kw[2] = widen3to4(__builtin_amdgcn_alignbit(a2, a1, 16));
+        kw[3] = widen3to4(a2 >> 8);
+      } else if constexpr (K3) {
+        const uint64_t x = ((((uint64_t)T.k[kb][1]) << 32) | T.k[kb][0]) >> sh3;
+        kw[0] = widen3to4((unsigned)x);
+        kw[1] = widen3to4((unsigned)(x >> 24));
+      } else {
+#pragma unroll
+        for (int w = 0; w < KW; ++w) kw[w] = T.k[kb][w];
+      }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         unsigned sel[4];
-        if constexpr (KBITS == 4) {
-          const unsigned w0 = T.k[kb][2 * kk], w1 = T.k[kb][2 * kk + 1];
+        if constexpr (KBITS >= 3) {
+          const unsigned w0 = kw[2 * kk], w1 = kw[2 * kk + 1];
           sel[0] = w0 & 0x0f0f0f0fu;
           sel[1] = (w0 >> 4) & 0x0f0f0f0fu;
           sel[2] = w1 & 0x0f0f0f0fu;
           sel[3] = (w1 >> 4) & 0x0f0f0f0fu;
         } else {
-          const unsigned w = T.k[kb][kk];
+          const unsigned w = kw[kk];
 #pragma unroll
           for (int c = 0; c < 4; ++c) sel[c] = (w >> (2 * c)) & 0x03030303u;
         }
@@ -455,7 +542,7 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
       for (int c = 0; c < FV; ++c) {
         unsigned sel[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sel[e] = ((unsigned)w4[e] >> (VBITS * c)) & (VBITS == 4 ? 0x0f0f0f0fu : 0x03030303u);
+        for (int e = 0; e < 4; ++e) sel[e] = ((unsigned)w4[e] >> (C::LV * c)) & (C::LV == 4 ? 0x0f0f0f0fu : 0x03030303u);
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
           const i32x4 av = {(int)lookup4<VBITS>(sel[0], vtab[t]), (int)lookup4<VBITS>(sel[1], vtab[t]),
@@ -614,6 +701,11 @@ hipError_t launch_tq_attn_bits(const TqAttnArgs& a, int kb, int vb, hipStream_t 
   if (kb == 4 && vb == 4) return launch_tq_attn_d<D, 4, 4>(a, st, name);
   if (kb == 2 && vb == 2) return launch_tq_attn_d<D, 2, 2>(a, st, name);
   if (kb == 2 && vb == 4) return launch_tq_attn_d<D, 2, 4>(a, st, name);
+  if (kb == 3 && vb == 3) return launch_tq_attn_d<D, 3, 3>(a, st, name);
+  if (kb == 3 && vb == 2) return launch_tq_attn_d<D, 3, 2>(a, st, name);
+  if (kb == 3 && vb == 4) return launch_tq_attn_d<D, 3, 4>(a, st, name);
+  if (kb == 4 && vb == 3) return launch_tq_attn_d<D, 4, 3>(a, st, name);
+  if (kb == 2 && vb == 3) return launch_tq_attn_d<D, 2, 3>(a, st, name);
   return hipErrorInvalidValue;
 }
 

@@ -312,3 +312,25 @@ def test_append_rope_arguments_checked_on_host(L):
     # misaligned table
     assert L.fa_append_kv_rope(p, p, 0, 4, 1, 128, p, 100, vp((1 << 20) + 4), p, p, p, p, p, None) == -1
     assert L.fa_append_kv_rope(p, p, 0, 4, 0, 128, p, 100, p, p, p, p, p, p, None) == 0   # no tokens: no-op
+
+
+def test_tq_attention_code_widths_checked_on_host(L):
+    """2-, 3- and 4-bit K and V codes pass the host checks (here stopped by the missing workspace,
+    before any HIP call); other widths and head dims are refused as unsupported."""
+    import numpy as np
+    vp = ctypes.c_void_p
+    p = vp(1 << 20)
+    books = {b: np.linspace(-1.0, 1.0, 1 << b).astype(np.float32) for b in (1, 2, 3, 4, 5)}
+
+    def call(kb, vb, d=128):
+        return L.fa_tq_attention_decode(p, 1, p, p, p, kb, vp(books[kb].ctypes.data), p, p, p, vb,
+                                        vp(books[vb].ctypes.data), p, 0, None, 8, 2, 100, d, 0.0, 0, 0, None, 0,
+                                        None, 0, None)
+
+    for kb in (2, 3, 4):
+        for vb in (2, 3, 4):
+            assert call(kb, vb) == -3 and "workspace" in fa.last_error(), (kb, vb)
+            assert call(kb, vb, d=64) == -3
+    for kb, vb in ((5, 3), (3, 1), (1, 2), (3, 5)):
+        assert call(kb, vb) == -2 and "2-, 3- or 4-bit" in fa.last_error()
+    assert call(3, 3, d=96) == -2 and "head_dim" in fa.last_error()

@@ -38,7 +38,7 @@ def _ref(q, host, **kw):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("kb,vb", [(4, 2), (4, 4), (2, 2), (2, 4)])
+@pytest.mark.parametrize("kb,vb", [(4, 2), (4, 4), (2, 2), (2, 4), (3, 3), (3, 2), (4, 3), (2, 3), (3, 4)])
 def test_tq_attention_matches_oracle_on_the_same_codes(d, kb, vb):
     import int8_compressed_kv_amd as fa
     torch_gpu()
@@ -85,16 +85,40 @@ def test_tq_attention_groups_fp32_query_window_and_short_caches(group):
     assert torch.equal(ob, o0.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("kind", ["sink16", "rising"])
-def test_tq_attention_long_cache_profiles(kind):
+@pytest.mark.parametrize("d", [64, 128])
+def test_tq_attention_three_bit_codes_short_caches_window_and_groups(d):
+    """3-bit codes straddle bytes: at head_dim 64 every other lane group's run starts 2 bytes into
+    a word, and the last run of a row ends at the row's (and, for the last key, the cache's) end.
+    Caches of 1 to 65 keys put that last key in every position of a tile."""
+    import int8_compressed_kv_amd as fa
+    torch_gpu()
+    for s_k in (1, 2, 37, 63, 64, 65):
+        for G in (1, 8):
+            say(f"tq attention 3-bit d={d} s_k={s_k} G={G}")
+            q, k, v = rng_normal(2800 + s_k + d + G, (2 * G, 1, d), (2, s_k, d), (2, s_k, d))
+            dev, host = _coded_cache(k, v, 3, 3, 2900 + s_k)
+            ref, lref = _ref(q, host)
+            out, lse = fa.tq_attention_decode(to_dev(q, "f32"), *dev, num_splits=3, return_lse=True)
+            check_close(to_np(out), ref, TOL_F32, f"3-bit d={d} s_k={s_k} G={G}")
+            check_close(to_np(lse), lref[:, 0], TOL_F32, "lse")
+    q, k, v = rng_normal(2990 + d, (8, 1, d), (2, 900, d), (2, 900, d))
+    q = round_bf16(q)
+    dev, host = _coded_cache(k, v, 3, 3, 2991)
+    refw, _ = _ref(q, host, window=130)
+    outw = fa.tq_attention_decode(to_dev(q, "bf16"), *dev, window=130)
+    check_close(to_np(outw), refw, TOL_F32, f"3-bit d={d} window 130")
+
+
+@pytest.mark.parametrize("kind,kb,vb", [("sink16", 4, 2), ("rising", 4, 2), ("sink16", 3, 3)])
+def test_tq_attention_long_cache_profiles(kind, kb, vb):
     """32768 keys (the long-cache decode length) with score profiles that stress the P~ digit
-    scale; K4/V2 codes, checked on all heads."""
+    scale, checked on all heads."""
     import int8_compressed_kv_amd as fa
     torch_gpu()
     d, bh_kv, G, s_k = 128, 2, 4, 32768
-    say(f"tq attention long cache {kind}")
+    say(f"tq attention long cache {kind} K{kb}/V{vb}")
     q, k, v = decode_profile_inputs(2600, bh_kv, G, s_k, d, kind)
-    dev, host = _coded_cache(k, v, 4, 2, 2700)
+    dev, host = _coded_cache(k, v, kb, vb, 2700)
     ref, _ = _ref(q, host)
     for splits in (2, 0):
         out = fa.tq_attention_decode(to_dev(q, "bf16"), *dev, num_splits=splits)
@@ -111,12 +135,16 @@ def test_tq_attention_quality_matches_the_quoted_cosines():
     q, k, v = rng_normal(61, (heads, 1, d), (heads, s_k, d), (heads, s_k, d))
     full, _ = oracle.attention(q, k, v, causal=False)
     gv = json.load(open(os.path.join(GOLDEN, "printed_values.json")))["turboquant_cosine"]
-    for kb, vb in ((4, 2), (4, 4)):
+    cosines = {}
+    for kb, vb in ((4, 2), (4, 3), (4, 4)):
         dev, _ = _coded_cache(k, v, kb, vb, 62)
         o = to_np(fa.tq_attention_decode(to_dev(q, "f32"), *dev))[:, 0]
         cos = float(np.mean(np.sum(o * full[:, 0], -1) / (np.linalg.norm(o, axis=-1) * np.linalg.norm(full[:, 0], axis=-1))))
         say(f"  K{kb}/V{vb} attention-output cosine vs unquantized: {cos:.4f}")
+        cosines[vb] = cos
         if vb == 2:
             assert abs(cos - gv["k4v2_synthetic"]) < 0.03
-        else:
+        elif vb == 4:
             assert cos > gv["k4v4"] - 0.01
+    # no printed figure for 3-bit V: its quality lies between the two quoted widths
+    assert cosines[2] < cosines[3] < cosines[4]
