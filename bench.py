@@ -16,6 +16,7 @@ Legs (each timed separately with HIP events on the stream the kernels run on):
   tqattn decode attention read straight from TurboQuant codes of the c4 cache (K 4-bit, V 2-bit,
          the page's default), 16 x 32 query / 8 KV heads, 32768 keys, d 128
   tqattn33 (not in the default set) the same with 3-bit K and V codes, which straddle bytes
+  tqattn_g8 (not in the default set) K4/V2 with a GQA group of 8 (16 x 64 query / 8 KV heads)
   merge  log-sum-exp merge of 8 key-chunk results for one 4096-row query chunk of the c5 shape
          (64 heads x 4096 rows, d 128, fp32 parts, bf16 output): the exchange of a ring prefill
   copy   (not in the default set) a plain 1 GiB device-to-device copy, the known-size reference
@@ -69,6 +70,7 @@ LEG_SOURCES = {
     "tq_dec": ("tq.hip", "device_common.hpp", "kernel_args.hpp"),
     "tqattn": ("tq_attn.hip", "device_common.hpp", "kernel_args.hpp"),
     "tqattn33": ("tq_attn.hip", "device_common.hpp", "kernel_args.hpp"),
+    "tqattn_g8": ("tq_attn.hip", "device_common.hpp", "kernel_args.hpp"),
 }
 
 
@@ -268,7 +270,7 @@ def main():
         del qd, kc, ks, vc, vs, out, q, k, v
 
     # ------------------------------------------------------------------ compress + decode c4
-    if legs & {"c4", "c4g8", "comp", "append", "tq", "tqattn", "tqattn33"}:
+    if legs & {"c4", "c4g8", "comp", "append", "tq", "tqattn", "tqattn33", "tqattn_g8"}:
         w = WORKLOADS["c4"]
         log(f"[bench] generating {w.name}")
         q, k, v = draw_qkv(w)
@@ -316,31 +318,34 @@ def main():
                              "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] tq decode: {avg:.3f} ms  {res['tq_dec']['gbs']:.0f} GB/s")
             del codes, norms, kb16, signs
-        for tq_leg, kbits, vbits in (("tqattn", 4, 2), ("tqattn33", 3, 3)):
+        for tq_leg, kbits, vbits, grp in (("tqattn", 4, 2, 4), ("tqattn33", 3, 3, 4), ("tqattn_g8", 4, 2, 8)):
             if tq_leg not in legs:
                 continue
             from synth_inputs import random_signs
+            # group 8: the c4 queries twice over, 64 query heads per batch against the same cache
+            q_t = qd if grp == 4 else torch.cat([qd, qd], 0)
+            bh_q_t = w.bh_kv * grp
             kcb, vcb = fa.tq_codebook(w.d, kbits), fa.tq_codebook(w.d, vbits)
             sk = torch.from_numpy(random_signs(64, w.d)).cuda()
             sv = torch.from_numpy(random_signs(65, w.d)).cuda()
             kcode, kn = fa.tq_encode(kf, sk, kbits, kcb)
             vcode, vn = fa.tq_encode(vf, sv, vbits, vcb)
-            out_t = torch.empty((w.bh_q, 1, w.d), dtype=torch.float32, device="cuda")
-            splits_t = int(fa.lib().fa_tq_attention_num_splits(w.bh_q, w.bh_kv, w.s_k, w.d))
-            ws_t = torch.empty(int(fa.lib().fa_tq_attention_workspace_bytes(w.bh_q, w.bh_kv, w.s_k, w.d, splits_t)),
+            out_t = torch.empty((bh_q_t, 1, w.d), dtype=torch.float32, device="cuda")
+            splits_t = int(fa.lib().fa_tq_attention_num_splits(bh_q_t, w.bh_kv, w.s_k, w.d))
+            ws_t = torch.empty(int(fa.lib().fa_tq_attention_workspace_bytes(bh_q_t, w.bh_kv, w.s_k, w.d, splits_t)),
                                dtype=torch.uint8, device="cuda")
-            fn = lambda: fa.tq_attention_decode(qd, kcode, kn, sk, kbits, kcb, vcode, vn, sv, vbits, vcb,   # noqa: E731
+            fn = lambda: fa.tq_attention_decode(q_t, kcode, kn, sk, kbits, kcb, vcode, vn, sv, vbits, vcb,   # noqa: E731
                                                 num_splits=splits_t, out=out_t, workspace=ws_t)
-            log(f"[bench] timing decode attention over TurboQuant codes (K{kbits}/V{vbits}, c4 shape)")
+            log(f"[bench] timing decode attention over TurboQuant codes (K{kbits}/V{vbits}, c4 cache, group {grp})")
             ms = timer.run(fn, args.steps, args.warmup, flush=flush)
             avg = float(np.mean(ms))
-            nbytes = n_tok * (w.d * kbits // 8 + 4 + w.d * vbits // 8 + 4) + w.bh_q * w.d * 2 + w.bh_q * w.d * 4
-            res[tq_leg] = {"workload": f"tq_attention_decode_k{kbits}v{vbits}_b16_h32kv8_sk32768_d128", "ms": avg,
+            nbytes = n_tok * (w.d * kbits // 8 + 4 + w.d * vbits // 8 + 4) + bh_q_t * w.d * 2 + bh_q_t * w.d * 4
+            res[tq_leg] = {"workload": f"tq_attention_decode_k{kbits}v{vbits}_b16_h{grp * 8}kv8_sk32768_d128", "ms": avg,
                            "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "num_splits": splits_t,
                            "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                            "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] {tq_leg}: {avg * 1e3:.1f} us  {res[tq_leg]['gbs']:.0f} GB/s")
-            del kcode, kn, vcode, vn, out_t, ws_t, sk, sv
+            del kcode, kn, vcode, vn, out_t, ws_t, sk, sv, q_t
         fa.compress_kv(kf, kc, ks)
         fa.compress_kv(vf, vc, vs)
         if "append" in legs:

@@ -26,7 +26,8 @@
 // Sums of digit products are exact integers; what is rounded is the codebook (to 21 fractional
 // bits of 2^E), q' and P~ (to 28 bits of their scale) and the fp32 recombination.
 //
-// Pass 1 (tq_attn_partial_kernel), grid (splits, bh_kv, ceil(G/4)): 4 waves stream 64-key tiles
+// Pass 1 (tq_attn_partial_kernel), one block per (split, bh_kv, group of 4 query heads), the
+// ceil(G/4) head groups of one key range on one XCD: 4 waves stream 64-key tiles
 // of one KV head (K codes straight into the MFMA operand layout, V codes through a wave-private
 // LDS slot for the transposing byte reads) and leave (m, l, O') per (query head, split).
 // Pass 2 (tq_attn_merge_kernel): per query head, the log-sum-exp merge of the splits, 1/l, the
@@ -165,9 +166,26 @@ void tq_attn_partial_kernel(TqAttnArgs a) {
   const int t_dig = n >> 2;
   const int gq = n & 3;
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int zh = blockIdx.z * HPW;
+  // block -> (split, KV head, group of 4 query heads).  The Z = ceil(G/4) slices of one (split, KV
+  // head) stream the same codes; they are dealt 8 blocks apart, so they land on one XCD (blocks go
+  // to the 8 XCDs in turn) at about the same time and the repeated reads can hit its L2.
+  const int Z = (a.group + HPW - 1) / HPW;
+  const int64_t n_chunk = (int64_t)a.num_splits * a.bh_kv;
+  const int64_t full = (n_chunk / 8) * 8 * Z;
+  const int64_t bid = blockIdx.x;
+  int64_t chunk;
+  int zs;
+  if (bid < full) {
+    const int64_t j = bid / 8;
+    chunk = 8 * (j / Z) + bid % 8;
+    zs = (int)(j % Z);
+  } else {
+    chunk = (n_chunk / 8) * 8 + (bid - full) / Z;
+    zs = (int)((bid - full) % Z);
+  }
+  const int split = (int)(chunk % a.num_splits);
+  const int kvh = (int)(chunk / a.num_splits);
+  const int zh = zs * HPW;
   const int nh = min(HPW, a.group - zh);
   const int64_t kv_base = (int64_t)kvh * a.s_k;
   const int head0 = kvh * a.group + zh;
@@ -684,7 +702,7 @@ hipError_t launch_tq_attn_d(const TqAttnArgs& a_in, hipStream_t st, const char**
   constexpr int KT = TqCfg<D, KB, VB>::KT;
   const int tiles = (a.s_k - a.key_lo + KT - 1) / KT;
   a.tiles_per_split = (tiles + a.num_splits - 1) / a.num_splits;
-  const dim3 grid((unsigned)a.num_splits, (unsigned)a.bh_kv, (unsigned)((a.group + 3) / 4));
+  const dim3 grid((unsigned)((int64_t)a.num_splits * a.bh_kv * ((a.group + 3) / 4)));
   const bool so = a.sops.n > 0;
   if (so) hipLaunchKernelGGL((tq_attn_partial_kernel<D, KB, VB, true>), grid, dim3(64 * kTqWaves), 0, st, a);
   else hipLaunchKernelGGL((tq_attn_partial_kernel<D, KB, VB, false>), grid, dim3(64 * kTqWaves), 0, st, a);
@@ -713,7 +731,7 @@ hipError_t launch_tq_attn_bits(const TqAttnArgs& a, int kb, int vb, hipStream_t 
 
 hipError_t launch_tq_attention(const TqAttnArgs& a, int32_t d, int32_t kbits, int32_t vbits, hipStream_t st,
                                const char** name) {
-  if (a.bh_kv > 65535 || (a.group + 3) / 4 > 65535) return hipErrorInvalidConfiguration;
+  if ((int64_t)a.num_splits * a.bh_kv * ((a.group + 3) / 4) > 0x7fffffff) return hipErrorInvalidConfiguration;
   switch (d) {
     case 64: return launch_tq_attn_bits<64>(a, kbits, vbits, st, name);
     case 128: return launch_tq_attn_bits<128>(a, kbits, vbits, st, name);

@@ -137,7 +137,7 @@ def test_decode_score_ops(d, group, chain):
     assert torch.equal(out2, out)
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 2), (2, 4)])
+@pytest.mark.parametrize("kb,vb", [(4, 2), (2, 4), (3, 3), (3, 4)])
 @pytest.mark.parametrize("chain", ["bias", "chain"])
 def test_tq_attention_score_ops(kb, vb, chain):
     import int8_compressed_kv_amd as fa
