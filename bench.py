@@ -236,7 +236,8 @@ def main():
             log(f"[bench] timing {ww.name}")
             ms = timer.run(fn, args.steps, args.warmup, settle=name != "c5")
             avg = float(np.mean(ms))
-            res[name] = {"workload": ww.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
+            res[name] = {"workload": ww.name, "ms": avg, "ms_min": float(np.min(ms)),
+                         "ms_median": float(np.median(ms)), "kernel": fa.last_kernel(),
                          "flop_per_launch": flops, "tflops": flops / avg / 1e9,
                          "frac_of_peak": flops / avg / 1e9 / PEAK_BF16_TFLOPS}
             log(f"[bench] {name}: {avg:.3f} ms  {res[name]['tflops']:.1f} TFLOP/s")
@@ -263,7 +264,8 @@ def main():
         log(f"[bench] timing {w.name}")
         ms = timer.run(fn, args.steps, args.warmup)
         avg = float(np.mean(ms))
-        res["c3"] = {"workload": w.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
+        res["c3"] = {"workload": w.name, "ms": avg, "ms_min": float(np.min(ms)), "ms_median": float(np.median(ms)),
+                     "kernel": fa.last_kernel(),
                      "flop_per_launch": flops, "tflops": flops / avg / 1e9,
                      "frac_of_peak": flops / avg / 1e9 / PEAK_BF16_TFLOPS}
         log(f"[bench] c3: {avg:.3f} ms  {res['c3']['tflops']:.1f} TFLOP/s")
@@ -288,7 +290,8 @@ def main():
             ms = timer.run(fn, args.steps, args.warmup, flush=flush)
             avg = float(np.mean(ms))
             nbytes = n_tok * w.d * 4 + n_tok * w.d + n_tok * 4
-            res["comp"] = {"workload": "compress_c4_k_cache_128x32768x128_f32", "ms": avg, "ms_min": float(np.min(ms)),
+            res["comp"] = {"workload": "compress_c4_k_cache_128x32768x128_f32", "ms": avg,
+                           "ms_min": float(np.min(ms)), "ms_median": float(np.median(ms)),
                            "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                            "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] comp: {avg:.3f} ms  {res['comp']['gbs']:.0f} GB/s")
@@ -304,7 +307,8 @@ def main():
             ms = timer.run(fn, args.steps, args.warmup, flush=flush)
             avg = float(np.mean(ms))
             nbytes = n_tok * (w.d * 4 + w.d * bits // 8 + 4)
-            res["tq"] = {"workload": "tq4_encode_c4_k_cache_128x32768x128_f32", "ms": avg, "ms_min": float(np.min(ms)),
+            res["tq"] = {"workload": "tq4_encode_c4_k_cache_128x32768x128_f32", "ms": avg,
+                         "ms_min": float(np.min(ms)), "ms_median": float(np.median(ms)),
                          "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                          "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] tq encode: {avg:.3f} ms  {res['tq']['gbs']:.0f} GB/s")
@@ -314,7 +318,8 @@ def main():
             avg = float(np.mean(ms))
             nbytes = n_tok * (w.d * bits // 8 + 4 + w.d * 2)
             res["tq_dec"] = {"workload": "tq4_decode_c4_k_cache_128x32768x128_to_bf16", "ms": avg,
-                             "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "bytes_per_launch": nbytes,
+                             "ms_min": float(np.min(ms)),
+                             "ms_median": float(np.median(ms)), "kernel": fa.last_kernel(), "bytes_per_launch": nbytes,
                              "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] tq decode: {avg:.3f} ms  {res['tq_dec']['gbs']:.0f} GB/s")
             del codes, norms, kb16, signs
@@ -340,8 +345,9 @@ def main():
             ms = timer.run(fn, args.steps, args.warmup, flush=flush)
             avg = float(np.mean(ms))
             nbytes = n_tok * (w.d * kbits // 8 + 4 + w.d * vbits // 8 + 4) + bh_q_t * w.d * 2 + bh_q_t * w.d * 4
-            res[tq_leg] = {"workload": f"tq_attention_decode_k{kbits}v{vbits}_b16_h{grp * 8}kv8_sk32768_d128", "ms": avg,
-                           "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "num_splits": splits_t,
+            res[tq_leg] = {"workload": f"tq_attention_decode_k{kbits}v{vbits}_b16_h{grp * 8}kv8_sk32768_d128",
+                           "ms": avg, "ms_min": float(np.min(ms)),
+                           "ms_median": float(np.median(ms)), "kernel": fa.last_kernel(), "num_splits": splits_t,
                            "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                            "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] {tq_leg}: {avg * 1e3:.1f} us  {res[tq_leg]['gbs']:.0f} GB/s")
@@ -360,6 +366,7 @@ def main():
             avg = float(np.mean(ms))
             nbytes = 2 * w.bh_kv * (w.d * 4 + w.d + 4) + w.bh_kv * 4
             res["append"] = {"workload": "append_c4_1tok_kv128_d128_f32", "ms": avg, "ms_min": float(np.min(ms)),
+                             "ms_median": float(np.median(ms)),
                              "kernel": fa.last_kernel(), "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                              "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS, "bound": "launch latency"}
             log(f"[bench] append: {avg * 1e3:.1f} us")
@@ -375,7 +382,8 @@ def main():
             ms = timer.run(fn, args.steps, args.warmup, flush=flush)
             avg = float(np.mean(ms))
             nbytes = (2 * w.bh_kv * w.s_k * w.d + 2 * w.bh_kv * w.s_k * 4 + w.bh_q * w.d * 2 + w.bh_q * w.d * 4)
-            res["c4"] = {"workload": w.name, "ms": avg, "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(),
+            res["c4"] = {"workload": w.name, "ms": avg, "ms_min": float(np.min(ms)),
+                         "ms_median": float(np.median(ms)), "kernel": fa.last_kernel(),
                          "num_splits": splits, "bytes_per_launch": nbytes, "gbs": nbytes / avg / 1e6,
                          "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] c4: {avg * 1e3:.1f} us  {res['c4']['gbs']:.0f} GB/s")
@@ -396,6 +404,7 @@ def main():
             avg = float(np.mean(ms))
             nbytes = (2 * w.bh_kv * w.s_k * w.d + 2 * w.bh_kv * w.s_k * 4 + bh_q8 * w.d * 2 + bh_q8 * w.d * 4)
             res["c4g8"] = {"workload": "decode_g8_b16_h64kv8_sk32768_d128", "ms": avg, "ms_min": float(np.min(ms)),
+                           "ms_median": float(np.median(ms)),
                            "kernel": fa.last_kernel(), "num_splits": splits8, "bytes_per_launch": nbytes,
                            "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
             log(f"[bench] c4g8: {avg * 1e3:.1f} us  {res['c4g8']['gbs']:.0f} GB/s")
@@ -415,7 +424,8 @@ def main():
         avg = float(np.mean(ms))
         nbytes = n_parts * rows * (d * 4 + 4) + rows * d * 2
         res["merge"] = {"workload": "merge_8parts_h64_4096rows_d128_f32_to_bf16", "ms": avg,
-                        "ms_min": float(np.min(ms)), "kernel": fa.last_kernel(), "bytes_per_launch": nbytes,
+                        "ms_min": float(np.min(ms)),
+                        "ms_median": float(np.median(ms)), "kernel": fa.last_kernel(), "bytes_per_launch": nbytes,
                         "gbs": nbytes / avg / 1e6, "frac_of_peak": nbytes / avg / 1e6 / PEAK_HBM_GBS}
         log(f"[bench] merge: {avg * 1e3:.1f} us  {res['merge']['gbs']:.0f} GB/s")
         del o_parts, lse_parts, out

@@ -142,8 +142,8 @@ def test_decode_score_ops(d, group, chain):
 def test_tq_attention_score_ops(kb, vb, chain):
     import int8_compressed_kv_amd as fa
     torch = torch_gpu()
-    say(f"score ops tq attention K{kb}/V{vb} {chain}")
-    d, bh_kv, G, s_k = 128, 2, 4, 1300
+    d, bh_kv, G, s_k = 128, 2, 8 if kb == 3 else 4, 1300   # group 8: two wave groups per block
+    say(f"score ops tq attention K{kb}/V{vb} {chain} G={G}")
     q, k, v = rng_normal(3400 + kb, (bh_kv * G, 1, d), (bh_kv, s_k, d), (bh_kv, s_k, d))
     q = round_bf16(q)
     sk, sv = random_signs(3401, d), random_signs(3402, d)

@@ -56,7 +56,7 @@ def test_tq_attention_matches_oracle_on_the_same_codes(d, kb, vb):
     assert fa.last_kernel() == "tq_attention_decode"
 
 
-@pytest.mark.parametrize("group", [1, 2, 8, 6])
+@pytest.mark.parametrize("group", [1, 2, 8, 6, 12, 16])
 def test_tq_attention_groups_fp32_query_window_and_short_caches(group):
     import int8_compressed_kv_amd as fa
     torch = torch_gpu()
