@@ -350,6 +350,19 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
       }
     }
   };
+  // one V^T fragment (keys 32 kb + 16 s2 + ..., head-dim block db), read just before its MFMA
+  // above head_dim 128, where a whole half tile of fragments would not fit the registers
+  auto vread1 = [&](const unsigned short* Vt, int kb, int s2, int db) __attribute__((always_inline)) {
+    const int krd = 32 * kb + 16 * s2 + 4 * (g16 >> 1) + (i16 >> 2);
+    const int d = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+    const int e0 = krd * D + 8 * ((d >> 3) ^ swz<SWZ>(krd)) + (d & 7);
+    const int e1 = (krd + 8) * D + 8 * ((d >> 3) ^ swz<SWZ>(krd + 8)) + (d & 7);
+    const u32x2 w0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e0)));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) unsigned short*)Vt + e1)));
+    return u32x4{w0[0], w0[1], w1[0], w1[1]};
+  };
 
   // one tile from operand stage `stage` (K~, V~ in fp16)
   auto compute = [&](const int t, auto stage) __attribute__((always_inline)) {
@@ -386,7 +399,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
 
     // V^T fragments of the first 32 keys, read while the softmax runs
     u32x4 vf0[2][NDB];
-    vread(Vt, 0, vf0);
+    if constexpr (D <= 128) vread(Vt, 0, vf0);
 
     if constexpr (SOPS) {
       // the ops act on S = S~ 2^es (exact power-of-two rescalings either way)
@@ -460,15 +473,19 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_i8kv_kernel(Prefil
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (D > 128) vf0[s2][db] = vread1(Vt, 0, s2, db);
         O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf0[s2][db]), __builtin_bit_cast(f16x8, Pw[0][s2]), O[db]);
+      }
     u32x4 vf1[2][NDB];
-    vread(Vt, 1, vf1);
+    if constexpr (D <= 128) vread(Vt, 1, vf1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (D > 128) vf1[s2][db] = vread1(Vt, 1, s2, db);
         O[db] = mfma32_f16(__builtin_bit_cast(f16x8, vf1[s2][db]), __builtin_bit_cast(f16x8, Pw[1][s2]), O[db]);
+      }
   };
 
   // converted 16-byte chunk (8 values) of row r, logical chunk lc, into operand stage st
