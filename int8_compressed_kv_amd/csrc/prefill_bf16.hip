@@ -438,6 +438,56 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       pair(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
       pair(t + 2, std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
     }
+  } else if constexpr (D > 128 && (BN * NC / 64) % NW == 0) {
+    // head_dim above 128 (4 waves): tile t + 1 is copied global -> LDS directly into the other of
+    // two stages while tile t is computed (no staging registers: a 256-wide tile would need 128),
+    // each wave waits for its own copies and one barrier per tile publishes them.  The copies
+    // follow the layout of the copies above: lane l of segment g fills 16-byte position 64 g + l
+    // with the logical chunk that belongs there; the last, partial tile clamps its rows.
+    constexpr int SPW = (BN * NC / 64) / NW;      // 1-KiB segments per wave per matrix
+    const unsigned lds_k0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned short*)&lds_k[0][0];
+    const unsigned lds_v0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned short*)&lds_v[0][0];
+    int crow[SPW], ccol[SPW];
+    unsigned voff[SPW], seg_k[SPW], seg_v[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int p = 64 * (SPW * wave + j) + lane;
+      crow[j] = p / NC;
+      ccol[j] = 8 * ((p % NC) ^ swz<SWZ>(p / NC));
+      voff[j] = 2u * (unsigned)(crow[j] * D + ccol[j]);
+      seg_k[j] = __builtin_amdgcn_readfirstlane(lds_k0 + 1024u * (unsigned)(SPW * wave + j));
+      seg_v[j] = __builtin_amdgcn_readfirstlane(lds_v0 + 1024u * (unsigned)(SPW * wave + j));
+    }
+    auto copy_tile = [&](int t, int st) {
+      const int k0 = (t_lo + t) * BN;
+      const unsigned st_off = 2u * C::TILE * (unsigned)st;
+      if (k0 + BN <= a.s_k) {
+        const unsigned short* kt = kp16 + (int64_t)k0 * D;
+        const unsigned short* vt = vp16 + (int64_t)k0 * D;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          copy16_to_lds(kt, voff[j], seg_k[j] + st_off);
+          copy16_to_lds(vt, voff[j], seg_v[j] + st_off);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+          const int64_t row = min(k0 + crow[j], a.s_k - 1);   // rows past the end repeat the last key
+          copy16_to_lds(kp16 + row * D + ccol[j], seg_k[j] + st_off);
+          copy16_to_lds(vp16 + row * D + ccol[j], seg_v[j] + st_off);
+        }
+      }
+    };
+    if (n_tiles > 0) copy_tile(0, 0);
+    wait_vmcnt0();
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int st = t & 1;
+      if (t + 1 < n_tiles) copy_tile(t + 1, st ^ 1);   // stage st^1 was last read before the previous barrier
+      compute(t, st);
+      wait_vmcnt0();
+      __syncthreads();
+    }
   } else {
     // the global loads of tile t + 1 are in flight (in registers) while tile t is computed
     auto step = [&](const int t, auto stage) {
