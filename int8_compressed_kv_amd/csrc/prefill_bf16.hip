@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
   constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, CH = C::CH;
   // head_dim 64 and 128: tiles arrive by direct global -> LDS copies into four stages, one
   // barrier per two tiles; other head dims stage through registers into two stages.
-  constexpr bool DMA = D <= 128 && (BN * NC / 64) % NW == 0;
+  constexpr bool DMA = D <= 128;
   constexpr int NST = DMA ? 4 : 2;
   constexpr int SWZ = C::SWZ;
   constexpr int NKS = D / 16;   // 16-deep k-steps of Q.K
@@ -371,7 +371,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
     // barrier that ends the compute of tiles t - 4 and t - 3 (their stages), and are waited for
     // before the barrier ending the compute of tiles t - 2 and t - 1; between barriers the waves
     // run two tiles unsynchronised
-    constexpr int SPW = (BN * NC / 64) / NW;      // 1-KiB segments per wave per matrix
+    // 1-KiB segments per matrix and tile, and per wave: where they do not divide evenly (head_dim
+    // 32 and 96) the first waves take SPW each and the rest take what is left, possibly none
+    constexpr int SEGS = BN * NC / 64;
+    constexpr int SPW = (SEGS + NW - 1) / NW;
     const unsigned short* kp = static_cast<const unsigned short*>(a.k) + kv_base * D;
     const unsigned short* vp = static_cast<const unsigned short*>(a.v) + kv_base * D;
     int crow[SPW], ccol[SPW];
@@ -401,12 +404,14 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
         const unsigned short* vt = vp + (int64_t)k0 * D;
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
+          if (SEGS % NW != 0 && SPW * wave + j >= SEGS) break;
           copy16_to_lds(kt, voff[j], seg_k[j] + st_off);
           copy16_to_lds(vt, voff[j], seg_v[j] + st_off);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
+          if (SEGS % NW != 0 && SPW * wave + j >= SEGS) break;
           const int64_t row = min(k0 + crow[j], last_key);   // rows past the end repeat the last key
           copy16_to_lds(kp + row * D + ccol[j], seg_k[j] + st_off);
           copy16_to_lds(vp + row * D + ccol[j], seg_v[j] + st_off);
