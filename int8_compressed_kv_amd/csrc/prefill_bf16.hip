@@ -15,10 +15,10 @@
 //     registers.  Two waves per SIMD: while one runs the softmax on the vector ALU the other
 //     keeps the matrix core busy.
 //   * K and V tiles of 64 keys live in LDS row-major, 16-byte chunks XOR-swizzled by row so
-//     that both operand reads below are free of bank conflicts.  Tiles are double-buffered:
-//     the global loads of tile t+1 are in flight (in registers) while tile t is computed, then
-//     written to the other LDS stage; one barrier per tile.  For head_dim <= 128 the tile loop
-//     is unrolled by two so that the stage is a compile-time constant in every LDS address.
+//     that both operand reads below are free of bank conflicts.  Tiles are copied global -> LDS
+//     directly (no staging registers): for head_dim <= 128 into four stages with one barrier per
+//     two tiles, the tile loop unrolled so that the stage is a compile-time constant in every LDS
+//     address; above 128 into two stages with one barrier per tile.
 //   * S^T = K Q^T (keys = MFMA rows, queries = columns) on v_mfma_f32_32x32x16_bf16: each
 //     query's scores sit in one lane pair, so the row max needs one exchange, and P^T in the
 //     accumulator layout is already the B operand of O^T += V^T P^T.  The V^T operand (8 keys
@@ -40,9 +40,6 @@ namespace {
 typedef short s16x4v __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4v lds_s16x4;
 
-// dword 3 of a raw buffer resource on gfx9-family parts (32-bit data format; no swizzle)
-constexpr int kBufferFlags = 0x00020000;
-
 template <int D>
 struct Cfg {
   static constexpr int NW = D <= 128 ? 8 : 4;    // waves per workgroup (2 or 1 per SIMD)
@@ -51,7 +48,6 @@ struct Cfg {
   static constexpr int NC = D / 8;               // 16-byte chunks per row
   static constexpr int TILE = BN * D;            // 16-bit elements per K or V tile
   static constexpr int SWZ = (NC % 16 == 0) ? 16 : (NC % 8 == 0) ? 8 : 4;   // swizzle span
-  static constexpr int CH = (BN * NC + 64 * NW - 1) / (64 * NW);   // chunks per thread per matrix
   static constexpr float kLazyLog2 = 8.0f;       // stale-max headroom, exp2 domain
 };
 
@@ -84,7 +80,7 @@ __device__ __forceinline__ void wait_vmcnt0() {
 template <int D, bool SOPS>
 __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(PrefillArgs a) {
   using C = Cfg<D>;
-  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC, CH = C::CH;
+  constexpr int NW = C::NW, BM = C::BM, BN = C::BN, NC = C::NC;
   // head_dim 64 and 128: tiles arrive by direct global -> LDS copies into four stages, one
   // barrier per two tiles; other head dims stage through registers into two stages.
   constexpr bool DMA = D <= 128;
@@ -95,7 +91,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
 
   __shared__ __attribute__((aligned(16))) unsigned short lds_k[NST][C::TILE];
   __shared__ __attribute__((aligned(16))) unsigned short lds_v[NST][C::TILE];
-  __shared__ float lds_red[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,45 +146,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
 
   const unsigned short* kp16 = static_cast<const unsigned short*>(a.k) + kv_base * D;
   const unsigned short* vp16 = static_cast<const unsigned short*>(a.v) + kv_base * D;
-
-  // ---- staging: tile rows k0 .. k0 + 63 are read as 16-byte chunks with buffer loads (a
-  // scalar resource per tile, based at row k0 and ending at the head's last key, plus a constant
-  // per-lane offset: no vector address arithmetic, and rows past the end read as zero -- those
-  // keys are masked in the softmax), double-buffered in registers, and written to LDS at row r,
-  // physical chunk lc ^ swz(r).
-  u32x4 kreg[CH], vreg[CH];
-  int soff[CH];
-#pragma unroll
-  for (int u = 0; u < CH; ++u) {
-    const int idx = min(tid + 64 * NW * u, BN * NC - 1);
-    soff[u] = ((idx / NC) * D + 8 * (idx % NC)) * 2;
-  }
-  auto load_tile = [&](int t) {
-    const int k0 = (t_lo + t) * BN;
-    const int64_t rem = (int64_t)(a.s_k - k0) * D * 2;
-    const int nrec = (int)(rem < 0x7fffffff ? rem : 0x7fffffff);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(kp16 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(vp16 + (int64_t)k0 * D), 0, nrec, kBufferFlags);
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      kreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, soff[u], 0, 0));
-      vreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, soff[u], 0, 0));
-    }
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = tid + 64 * NW * u;
-      if (BN * NC % (64 * NW) == 0 || idx < BN * NC) {
-        const int r = idx / NC, lc = idx % NC;
-        const int pc = lc ^ swz<SWZ>(r);
-        *reinterpret_cast<u32x4*>(lds_k[st] + r * D + 8 * pc) = kreg[u];
-        *reinterpret_cast<u32x4*>(lds_v[st] + r * D + 8 * pc) = vreg[u];
-      }
-    }
-  };
 
   // ---- per-wave state
   f32x16 O[NDB];
@@ -443,7 +399,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       pair(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
       pair(t + 2, std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
     }
-  } else if constexpr (D > 128 && (BN * NC / 64) % NW == 0) {
+  } else {
+    static_assert((BN * NC / 64) % NW == 0, "whole 1-KiB copy segments per wave");
     // head_dim above 128 (4 waves): tile t + 1 is copied global -> LDS directly into the other of
     // two stages while tile t is computed (no staging registers: a 256-wide tile would need 128),
     // each wave waits for its own copies and one barrier per tile publishes them.  The copies
@@ -492,31 +449,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::NW, 1) void prefill_bf16_kernel(Prefil
       compute(t, st);
       wait_vmcnt0();
       __syncthreads();
-    }
-  } else {
-    // the global loads of tile t + 1 are in flight (in registers) while tile t is computed
-    auto step = [&](const int t, auto stage) {
-      const int st = static_cast<int>(stage);
-      load_tile(min(t + 1, n_tiles - 1));
-      compute(t, stage);
-      if (t + 1 < n_tiles) store_tile(st ^ 1);   // stage st^1 was last read before the previous barrier
-      __syncthreads();
-    };
-    if (n_tiles > 0) {
-      load_tile(0);
-      store_tile(0);
-    }
-    __syncthreads();
-    if constexpr (D <= 128) {
-      int t = 0;
-      for (; t + 1 < n_tiles; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        step(t + 1, std::integral_constant<int, 1>{});
-      }
-      if (t < n_tiles) step(t, std::integral_constant<int, 0>{});
-    } else {
-      // wider heads already use the whole register file; the stage stays a loop variable
-      for (int t = 0; t < n_tiles; ++t) step(t, t & 1);
     }
   }
 
